@@ -1,0 +1,149 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) paged MLA decode library.
+ *
+ * The operation (restated from the FlashInfer API docs page
+ * "flashinfer.attention.prims_ts.prims_ts_batch_decode_with_kv_cache_mla",
+ * signature and the layout/mask and contract paragraphs; scale semantics from
+ * FlashInfer PR #1248 "update cubins for dynamic scale factor interface and
+ * one-copy kvcache on trtllm-gen mla", Highlights; one-copy K/V from FlashInfer
+ * issue #3131 "Support cum_seq_lens_q in trtllm_batch_decode_with_kv_cache_mla
+ * trtllm-gen backend", run_func excerpt; natural-log LSE from the vLLM docs page
+ * "FlashInferMLAImpl", class attributes):
+ *
+ *   For request b with live KV length L = seq_lens[b] and query rows
+ *   i = 0 .. q_b-1, and every head h:
+ *     s[j]   = bmm1_scale * dot(q[r_b+i, h, 0:576], K[j, 0:576]),  j < n
+ *     out[r_b+i, h, 0:512] = bmm2_scale * sum_j softmax(s)[j] * K[j, 0:512]
+ *     lse[r_b+i, h]        = ln(sum_j exp(s[j]))          (no bmm2 inside)
+ *   K[j] is cache row (block_tables[b, j / page_size], j % page_size); the same
+ *   rows serve as values (their first 512 dims).  n = L - q_b + i + 1 when
+ *   causal (bottom-right aligned), n = L otherwise.
+ *
+ * Everything here is asynchronous on the caller's HIP stream; nothing reads
+ * device memory back to the host, nothing allocates, nothing synchronises.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Any code other than MLA_OK means nothing was enqueued. */
+enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_POINTER = 1,      /* a required pointer is NULL */
+  MLA_ERR_BAD_HEADS = 2,         /* num_heads <= 0 or not a multiple of 16 */
+  MLA_ERR_BAD_PAGE_SIZE = 3,     /* page_size not in {16, 32, 64} */
+  MLA_ERR_BAD_HEAD_DIMS = 4,     /* kv_lora_rank != 512 or qk_rope_head_dim != 64 */
+  MLA_ERR_BAD_DTYPE = 5,         /* kv_dtype not MLA_KV_BF16 / MLA_KV_FP8_E4M3FN */
+  MLA_ERR_MISALIGNED = 6,        /* q, kv_cache, out or workspace not 16-byte aligned */
+  MLA_ERR_WORKSPACE_TOO_SMALL = 7,
+  MLA_ERR_BAD_Q_LEN = 8,         /* max_q_len < 1, fixed launch with q_len_fixed != max_q_len,
+                                    or total_q inconsistent with a fixed launch */
+  MLA_ERR_BAD_BLOCK_TABLE = 9,   /* block_table_stride * page_size < max_seq_len */
+  MLA_ERR_BAD_SHAPE = 10,        /* batch out of [1, MLA_MAX_BATCH], max_seq_len < 1, num_pages < 1 */
+  MLA_ERR_HIP = 11,              /* the HIP runtime reported an error at launch */
+  MLA_ERR_NO_DEVICE = 12         /* no usable gfx950 device is current */
+};
+
+enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3FN = 1 };
+
+/* Largest batch one launch accepts (the work plan lives in LDS). */
+#define MLA_MAX_BATCH 1024
+
+/* Static shape of a launch.  All fields are host integers. */
+typedef struct mla_decode_dims {
+  int32_t batch;              /* B: requests */
+  int32_t num_heads;          /* H: query heads (all share the one latent KV head) */
+  int32_t q_len_fixed;        /* SQ for a fixed [B, SQ, H, 576] query; ignored when packed */
+  int32_t total_q;            /* rows of q / out / lse (B*SQ, or qo_indptr[B] when packed) */
+  int32_t page_size;          /* rows per cache page: 16, 32 or 64 */
+  int64_t num_pages;          /* pages in kv_cache (page ids must be < num_pages) */
+  int32_t block_table_stride; /* W: int32 entries per block_tables row */
+  int32_t kv_dtype;           /* MLA_KV_BF16 or MLA_KV_FP8_E4M3FN */
+  int32_t kv_lora_rank;       /* must be 512 */
+  int32_t qk_rope_head_dim;   /* must be 64 */
+} mla_decode_dims_t;
+
+/*
+ * mla_decode_paged -- enqueue one batched paged MLA decode on `stream`.
+ *
+ * q            device, bf16 [total_q, H, 576] row-major (a fixed [B, SQ, H, 576]
+ *              query is the same bytes).  Dims 0..511 latent, 512..575 RoPE.
+ * kv_cache     device, [num_pages, page_size, 576] (bf16, or fp8 E4M3FN bytes);
+ *              a [num_pages, 1, page_size, 576] view is the same bytes.  Row j of
+ *              request b is read only for j < seq_lens[b]; other slots may hold
+ *              anything, NaN included, and never affect the result.
+ * block_tables device, int32 [B, block_table_stride] row-major.  Only entries
+ *              0 .. ceil(seq_lens[b]/page_size)-1 of row b are read.
+ * seq_lens     device, int32 [B]; each in [1, max_seq_len].
+ * qo_indptr    device, int32 [B+1] cumulative query offsets (starts at 0, strictly
+ *              increasing, ends at total_q, deltas <= max_q_len), or NULL for a
+ *              fixed launch where every request has q_len_fixed rows.
+ * max_seq_len  static bound on seq_lens (sizes only; never changes results).
+ * max_q_len    static bound on per-request query length (sizes only).
+ * bmm1_scale   complete logit multiplier (softmax scale x q/k dequant scales).
+ * bmm2_scale   output multiplier (v dequant scale x output scale).
+ * causal       nonzero: bottom-right causal mask; zero: every row sees all L rows.
+ *              Causal launches need q_b <= seq_lens[b].
+ * out          device, bf16 [total_q, H, 512], written completely.
+ * lse          device, float32 [total_q, H] natural-log LSE, or NULL for none.
+ * workspace    device scratch of at least mla_decode_paged_workspace_size() bytes,
+ *              16-byte aligned, exclusive to this launch until it completes, and
+ *              not overlapping any other argument.  It needs no initialisation
+ *              and holds nothing between launches.
+ * dims         host pointer to the static shape above (read during the call only).
+ * stream       hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Ownership: every pointer stays owned by the caller; the library keeps none
+ * after the enqueued work completes and allocates nothing per call.  The first
+ * call on a device caches its compute-unit count; call once before capturing
+ * a HIP graph.  Device-resident contract violations (lengths, offsets, page
+ * ids out of range) are not checked and give undefined results.
+ * Returns MLA_OK or an MLA_ERR_* code (then nothing was enqueued, except
+ * MLA_ERR_HIP, which reports a launch failure).
+ */
+int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_tables,
+                     const int32_t* seq_lens, const int32_t* qo_indptr, int32_t max_seq_len,
+                     int32_t max_q_len, float bmm1_scale, float bmm2_scale, int causal, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes,
+                     const mla_decode_dims_t* dims, void* stream);
+
+/*
+ * Bytes of workspace mla_decode_paged needs for this shape on the current
+ * device (depends on its compute-unit count).  Returns 0 for a shape that
+ * mla_decode_paged would reject.  want_lse is accepted for symmetry; the size
+ * does not depend on it.
+ */
+size_t mla_decode_paged_workspace_size(const mla_decode_dims_t* dims, int32_t max_seq_len,
+                                       int32_t max_q_len, int want_lse);
+
+/* Static, NUL-terminated description of a status code. */
+const char* mla_status_string(int status);
+
+/*
+ * Test hook, not part of the serving interface: override the persistent grid
+ * size (workgroups) used to split work, 0 restores the default (one workgroup
+ * per compute unit).  Changes how KV ranges are split and merged, never the
+ * result beyond rounding.  Affects later calls and workspace sizes on every
+ * device; not thread-safe against concurrent launches.
+ */
+void mla_decode_internal_set_grid_override(int32_t grid);
+
+/*
+ * Test hook, not part of the serving interface: widen n_groups x 8 fp8 E4M3FN
+ * codes (device, 8-byte aligned) to bf16 (device, 16-byte aligned) with the
+ * exact conversion the decode kernel applies to an fp8 cache, on `stream`.
+ * Returns MLA_OK, MLA_ERR_NULL_POINTER, MLA_ERR_MISALIGNED or MLA_ERR_HIP.
+ */
+int mla_decode_internal_fp8_to_bf16(const void* in, void* out, int64_t n_groups, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

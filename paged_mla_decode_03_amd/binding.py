@@ -1,0 +1,204 @@
+"""Thin ctypes binding over the C ABI in include/mla_decode.h.
+
+Argument marshalling only: every step of the decode runs in the HIP library.
+torch supplies device memory and the current HIP stream.  Nothing here falls
+back to a CPU path: if the library is missing, every call raises.
+
+Interface modelled on FlashInfer's paged MLA decode API (docs page
+"flashinfer.attention.prims_ts.prims_ts_batch_decode_with_kv_cache_mla",
+signature and contract): fixed [B, SQ, H, 576] or packed [total_q, H, 576]
+queries with qo_indptr, a [pages, page_size, 576] (or [pages, 1, page_size, 576])
+cache, block_tables / seq_lens, caller-owned workspace, optional preallocated
+output, bmm1/bmm2 scales and a causal or dense mask.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+
+MLA_OK = 0
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3FN = 1
+KV_LORA_RANK = 512
+QK_ROPE_HEAD_DIM = 64
+D_QK = KV_LORA_RANK + QK_ROPE_HEAD_DIM
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("q_len_fixed", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("block_table_stride", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32),
+        ("qk_rope_head_dim", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Load the HIP library once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.mla_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, sz,
+                                     ctypes.POINTER(MlaDims), vp]
+    lib.mla_decode_paged.restype = ctypes.c_int
+    lib.mla_decode_paged_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int]
+    lib.mla_decode_paged_workspace_size.restype = sz
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_decode_internal_set_grid_override.argtypes = [i32]
+    lib.mla_decode_internal_set_grid_override.restype = None
+    lib.mla_decode_internal_fp8_to_bf16.argtypes = [vp, vp, i64, vp]
+    lib.mla_decode_internal_fp8_to_bf16.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def mla_status_string(status):
+    return load_library().mla_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def make_dims(*, batch, num_heads, q_len_fixed, total_q, page_size, num_pages, block_table_stride, kv_dtype,
+              kv_lora_rank=KV_LORA_RANK, qk_rope_head_dim=QK_ROPE_HEAD_DIM):
+    return MlaDims(batch, num_heads, q_len_fixed, total_q, page_size, num_pages, block_table_stride, kv_dtype,
+                   kv_lora_rank, qk_rope_head_dim)
+
+
+def mla_decode_paged_workspace_size(dims, max_seq_len, max_q_len, want_lse=False):
+    return int(load_library().mla_decode_paged_workspace_size(ctypes.byref(dims), int(max_seq_len),
+                                                             int(max_q_len), int(bool(want_lse))))
+
+
+def mla_decode_paged(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q_len, bmm1_scale,
+                     bmm2_scale, causal, out, lse, workspace, workspace_bytes, dims, stream=None):
+    """Direct call of the C entry point (tensors or raw device pointers). Returns the status."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().mla_decode_paged(
+        _ptr(q), _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(qo_indptr), int(max_seq_len),
+        int(max_q_len), float(bmm1_scale), float(bmm2_scale), int(bool(causal)), _ptr(out), _ptr(lse),
+        _ptr(workspace), int(workspace_bytes), ctypes.byref(dims), stream))
+
+
+def set_grid_override(grid):
+    """Test hook: force the persistent grid size (0 = one workgroup per CU)."""
+    load_library().mla_decode_internal_set_grid_override(int(grid))
+
+
+def fp8_to_bf16_device(codes):
+    """Test hook: widen a uint8 device tensor of fp8 E4M3FN codes (length a
+    multiple of 8) to bf16 with the kernel's own conversion."""
+    assert codes.dtype == torch.uint8 and codes.is_cuda and codes.numel() % 8 == 0
+    out = torch.empty(codes.numel(), dtype=torch.bfloat16, device=codes.device)
+    rc = load_library().mla_decode_internal_fp8_to_bf16(codes.data_ptr(), out.data_ptr(), codes.numel() // 8,
+                                                       torch.cuda.current_stream().cuda_stream)
+    if rc != MLA_OK:
+        raise RuntimeError(mla_status_string(rc))
+    return out
+
+
+def _kv_code(dtype):
+    if dtype == torch.bfloat16:
+        return MLA_KV_BF16
+    if dtype == torch.float8_e4m3fn:
+        return MLA_KV_FP8_E4M3FN
+    raise TypeError(f"kv_cache dtype {dtype} not supported (bf16 or float8_e4m3fn)")
+
+
+def dims_for(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len_q):
+    if kv_cache.dim() == 4:
+        if kv_cache.shape[1] != 1:
+            raise ValueError("rank-4 kv_cache must be [pages, 1, page_size, 576]")
+        kv_cache = kv_cache.squeeze(1)
+    if kv_cache.dim() != 3 or kv_cache.shape[-1] != D_QK:
+        raise ValueError("kv_cache must be [pages, page_size, 576]")
+    B = int(seq_lens.shape[0])
+    if qo_indptr is None:
+        if query.dim() != 4 or query.shape[0] != B:
+            raise ValueError("fixed launch needs query [B, SQ, H, 576]")
+        sq, H = int(query.shape[1]), int(query.shape[2])
+        total_q = B * sq
+        max_q = sq
+    else:
+        if query.dim() != 3:
+            raise ValueError("packed launch needs query [total_q, H, 576]")
+        if max_seq_len_q is None:
+            raise ValueError("max_seq_len_q is required with qo_indptr")
+        total_q, H = int(query.shape[0]), int(query.shape[1])
+        sq = int(max_seq_len_q)
+        max_q = int(max_seq_len_q)
+    dims = make_dims(batch=B, num_heads=H, q_len_fixed=sq, total_q=total_q, page_size=int(kv_cache.shape[1]),
+                     num_pages=int(kv_cache.shape[0]), block_table_stride=int(block_tables.shape[1]),
+                     kv_dtype=_kv_code(kv_cache.dtype))
+    return dims, max_q, total_q, H
+
+
+def workspace_bytes_for(query, kv_cache, block_tables, seq_lens, max_seq_len, *, qo_indptr=None,
+                        max_seq_len_q=None, return_lse=False):
+    dims, max_q, _, _ = dims_for(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len_q)
+    n = mla_decode_paged_workspace_size(dims, max_seq_len, max_q, return_lse)
+    if n == 0:
+        raise ValueError("shape rejected by the library (see mla_decode_paged status codes)")
+    return n
+
+
+def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_len, *, qo_indptr=None,
+           max_seq_len_q=None, out=None, lse=None, return_lse=False, bmm1_scale=1.0, bmm2_scale=1.0,
+           causal=True):
+    """Batched paged MLA decode.  Returns out, or (out, lse) with return_lse."""
+    for name, t in (("query", query), ("kv_cache", kv_cache), ("workspace_buffer", workspace_buffer),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if query.dtype != torch.bfloat16:
+        raise TypeError("query must be bfloat16")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if qo_indptr is not None and (qo_indptr.dtype != torch.int32 or not qo_indptr.is_cuda):
+        raise TypeError("qo_indptr must be an int32 device tensor")
+    dims, max_q, total_q, H = dims_for(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len_q)
+    out_shape = tuple(query.shape[:-1]) + (KV_LORA_RANK,)
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.bfloat16, device=query.device)
+    elif tuple(out.shape) != out_shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {out_shape}")
+    if return_lse:
+        lse_shape = tuple(query.shape[:-1])
+        if lse is None:
+            lse = torch.empty(lse_shape, dtype=torch.float32, device=query.device)
+        elif tuple(lse.shape) != lse_shape or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError(f"lse must be a contiguous float32 tensor of shape {lse_shape}")
+    else:
+        lse = None
+    ws_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
+    rc = mla_decode_paged(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q, bmm1_scale,
+                          bmm2_scale, causal, out, lse, workspace_buffer, ws_bytes, dims)
+    if rc != MLA_OK:
+        raise RuntimeError(f"mla_decode_paged failed: {mla_status_string(rc)} (status {rc})")
+    return (out, lse) if return_lse else out

@@ -1,0 +1,84 @@
+"""Shared helpers for the GPU parity tests: run the HIP path on a seeded
+workload and compare with the float64 oracle on the same inputs."""
+
+import numpy as np
+import torch
+
+import oracle
+from paged_mla_decode_03_amd import binding
+from paged_mla_decode_03_amd.inputs import to_device_tensors
+
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+def run_hip(w, *, return_lse=None, out=None, kv_rank4=False, stream=None):
+    """Run the library on workload w.  Returns (out float32 [R, H, 512], lse float32 [R, H] or None)."""
+    t = to_device_tensors(w, "cuda")
+    B, H = w.batch, w.num_heads
+    q = t["q"]
+    if w.qo_indptr is None:
+        q = q.view(B, w.q_len_fixed, H, 576)
+    kv = t["kv"]
+    if kv_rank4:
+        kv = kv.unsqueeze(1)
+    want_lse = w.want_lse if return_lse is None else return_lse
+    nbytes = binding.workspace_bytes_for(q, kv, t["block_tables"], t["seq_lens"], w.max_seq_len,
+                                         qo_indptr=t["qo_indptr"], max_seq_len_q=w.max_q_len,
+                                         return_lse=want_lse)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    res = binding.decode(q, kv, ws, t["block_tables"], t["seq_lens"], w.max_seq_len, qo_indptr=t["qo_indptr"],
+                         max_seq_len_q=w.max_q_len if w.qo_indptr is not None else None, out=out,
+                         return_lse=want_lse, bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale, causal=w.causal)
+    torch.cuda.synchronize()
+    o, l = res if want_lse else (res, None)
+    o = o.float().reshape(w.total_q, H, 512).cpu().numpy()
+    l = None if l is None else l.reshape(w.total_q, H).cpu().numpy()
+    return o, l
+
+
+def oracle_rows(w, requests):
+    prob = oracle.MlaProblem(**w.oracle_problem_kwargs())
+    out, lse = oracle.reference_decode(prob, requests=requests)
+    rows = []
+    for b in requests:
+        r0, qb = prob.request_rows(b)
+        rows.extend(range(r0, r0 + qb))
+    return out, lse, np.array(rows, dtype=np.int64)
+
+
+def check_close(got, ref, what, atol=ATOL, rtol=RTOL):
+    """Elementwise |got - ref| <= atol + rtol*|ref| (the parity bar), plus a
+    relative-RMS bug signal far below it."""
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got.astype(np.float64) - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} elements outside tolerance; "
+                           f"max err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}")
+    rms = np.sqrt((err ** 2).mean()) / max(np.sqrt((ref ** 2).mean()), 1e-30)
+    return float(rms), float(err.max())
+
+
+def compare_with_oracle(w, requests=None, *, rel_rms_limit=5e-3, **run_kw):
+    if requests is None:
+        requests = list(range(w.batch))
+    got_o, got_l = run_hip(w, **run_kw)
+    ref_o, ref_l, rows = oracle_rows(w, requests)
+    rms, mx = check_close(got_o[rows], ref_o[rows], f"{w.name} out")
+    assert rms < rel_rms_limit, f"{w.name}: out relative RMS {rms:.2e} above the bf16 bug signal"
+    stats = {"out_rel_rms": rms, "out_max_err": mx}
+    if got_l is not None:
+        lrms, lmx = check_close(got_l[rows], ref_l[rows], f"{w.name} lse")
+        stats.update(lse_rel_rms=lrms, lse_max_err=lmx)
+    return stats
+
+
+def sample_requests(w, k=4, seed=0):
+    L = w.seq_lens
+    picks = {int(np.argmin(L)), int(np.argmax(L)), 0, w.batch - 1}
+    rng = np.random.default_rng(seed)
+    while len(picks) < min(w.batch, k + 2):
+        picks.add(int(rng.integers(w.batch)))
+    return sorted(picks)
