@@ -1,0 +1,190 @@
+"""Throughput benchmark: batched paged MLA decode on one MI355X.
+
+One step = one mla_decode_paged call (device work plan + decode kernel +
+split merge) over the whole batch of the DeepSeek-V3-shaped bf16 decode
+workload (B=64, H=128, q_len=1, 576/512 dims, seq_lens uniform in
+[1024, 8192], page size 64, shuffled pages), inputs resident in HBM.
+
+Prints one JSON line with the metric (KV-tokens/s), TFLOP/s, algorithmic
+GB/s, the decode kernel's roofline fraction (timed with HIP events on the
+launch stream) and the float64 CPU oracle's throughput on a bounded sample of
+the same workload.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+                  [--no-cpu-baseline] [--all]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged MLA decode KV-tokens/s and TFLOP/s at 1 GPU; % of MFMA/HBM roofline"
+DEFAULT_WORKLOAD = "dsv3_bf16_decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """Time the oracle as it stands on whole requests of w until ~budget_s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    prob = oracle.MlaProblem(**w.oracle_problem_kwargs())
+    done, tokens = [], 0
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        oracle.reference_decode(prob, requests=[b])
+        done.append(b)
+        tokens += int(w.seq_lens[b])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"requests 0..{done[-1]} of {w.name} ({len(done)} of {w.batch} requests, "
+                      f"{tokens} KV tokens, {dt:.1f} s, float64 NumPy)"}
+
+
+def run_workload(name, steps, warmup, want_cpu):
+    import numpy as np
+    import torch
+    from paged_mla_decode_03_amd import binding
+    from paged_mla_decode_03_amd.inputs import named_workload, to_device_tensors, WORKLOADS
+    from paged_mla_decode_03_amd.metrics import counts_for_workload, PEAK_HBM_GBS, PEAK_MFMA_TFLOPS
+
+    log(f"[bench] generating workload {name}")
+    w = named_workload(name, poison=False)
+    counts = counts_for_workload(w)
+    t = to_device_tensors(w, "cuda")
+    B, H = w.batch, w.num_heads
+    q = t["q"] if w.qo_indptr is not None else t["q"].view(B, w.q_len_fixed, H, 576)
+    max_q = w.max_q_len if w.qo_indptr is not None else None
+    nbytes = binding.workspace_bytes_for(q, t["kv"], t["block_tables"], t["seq_lens"], w.max_seq_len,
+                                         qo_indptr=t["qo_indptr"], max_seq_len_q=max_q, return_lse=w.want_lse)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(tuple(q.shape[:-1]) + (512,), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device="cuda") if w.want_lse else None
+
+    # validate once through the checked wrapper, then time the raw C entry point
+    binding.decode(q, t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, qo_indptr=t["qo_indptr"],
+                   max_seq_len_q=max_q, out=out, lse=lse, return_lse=w.want_lse, bmm1_scale=w.bmm1_scale,
+                   bmm2_scale=w.bmm2_scale, causal=w.causal)
+    dims, max_q_len, _, _ = binding.dims_for(q, t["kv"], t["block_tables"], t["seq_lens"], t["qo_indptr"], max_q)
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), t["kv"].data_ptr(), t["block_tables"].data_ptr(), t["seq_lens"].data_ptr(),
+            None if t["qo_indptr"] is None else t["qo_indptr"].data_ptr(), w.max_seq_len, max_q_len, w.bmm1_scale,
+            w.bmm2_scale, w.causal, out.data_ptr(), None if lse is None else lse.data_ptr(), ws.data_ptr(),
+            nbytes, dims, stream)
+
+    def step():
+        rc = binding.mla_decode_paged(*args)
+        if rc != 0:
+            raise RuntimeError(binding.mla_status_string(rc))
+
+    log(f"[bench] warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # decode-kernel events, recorded by the library on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        binding.set_kernel_events(ev[i][0], ev[i][1])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    binding.set_kernel_events(None, None)
+    ms_step = (t1 - t0) * 1e3 / steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    kv_bytes_per = 2 if w.kv_dtype == "bf16" else 1
+    dtype = "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma"
+    t_hbm = counts["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_mfma = counts["flops"] / (PEAK_MFMA_TFLOPS["bf16"] * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = counts["bytes"] / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+    else:
+        achieved = counts["flops"] / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": achieved / PEAK_MFMA_TFLOPS["bf16"], "traffic": None}
+    spec = WORKLOADS[name]
+    res = {
+        "metric": METRIC,
+        "value": counts["kv_tokens"] / (ms_step * 1e-3),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if kv_bytes_per == 2 else dtype,
+        "data": "synthetic (seeded N(0,1) bf16 q/kv, shuffled pages)",
+        "config": {"workload": name, "batch": B, "heads": H,
+                   "q_len": spec.get("q_len") if "q_len_range" not in spec else list(spec["q_len_range"]),
+                   "seq_lens": list(spec["seq_len_range"]) if "seq_len_range" in spec else
+                   (list(spec["seq_len_loguniform"]) if "seq_len_loguniform" in spec else spec.get("seq_lens")),
+                   "page_size": w.page_size, "kv_dtype": w.kv_dtype, "causal": w.causal, "lse": w.want_lse,
+                   "kv_tokens": counts["kv_tokens"]},
+        "tflops": counts["flops"] / (ms_step * 1e-3) / 1e12,
+        "gbps": counts["bytes"] / (ms_step * 1e-3) / 1e9,
+        "decode_kernel_ms": kern_ms,
+        "roofline": roof,
+    }
+    if want_cpu:
+        log("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(w)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads (lines on stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the decode path is single-GPU by design", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    res = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
+    if args.all:
+        from paged_mla_decode_03_amd.inputs import WORKLOAD_ORDER
+        for name in WORKLOAD_ORDER:
+            if name == args.workload:
+                continue
+            r = run_workload(name, args.steps, args.warmup, False)
+            log("[bench-extra] " + json.dumps(r))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -135,6 +135,15 @@ const char* mla_status_string(int status);
 void mla_decode_internal_set_grid_override(int32_t grid);
 
 /*
+ * Measurement hook, not part of the serving interface: when both are non-NULL,
+ * later mla_decode_paged calls record start_event (a hipEvent_t) on their stream
+ * right before the decode kernel and stop_event right after it, before the split
+ * merge, so a caller can time the decode kernel alone.  NULL, NULL turns it off.
+ * The events stay owned by the caller.
+ */
+void mla_decode_internal_set_kernel_events(void* start_event, void* stop_event);
+
+/*
  * Test hook, not part of the serving interface: widen n_groups x 8 fp8 E4M3FN
  * codes (device, 8-byte aligned) to bf16 (device, 16-byte aligned) with the
  * exact conversion the decode kernel applies to an fp8 cache, on `stream`.

@@ -64,6 +64,8 @@ def load_library():
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_decode_internal_set_grid_override.argtypes = [i32]
     lib.mla_decode_internal_set_grid_override.restype = None
+    lib.mla_decode_internal_set_kernel_events.argtypes = [vp, vp]
+    lib.mla_decode_internal_set_kernel_events.restype = None
     lib.mla_decode_internal_fp8_to_bf16.argtypes = [vp, vp, i64, vp]
     lib.mla_decode_internal_fp8_to_bf16.restype = ctypes.c_int
     _lib = lib
@@ -107,6 +109,16 @@ def mla_decode_paged(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len
 def set_grid_override(grid):
     """Test hook: force the persistent grid size (0 = one workgroup per CU)."""
     load_library().mla_decode_internal_set_grid_override(int(grid))
+
+
+def set_kernel_events(start_event, stop_event):
+    """Measurement hook: record two torch.cuda.Event (HIP events) around the
+    decode kernel of every later call; (None, None) turns it off."""
+    lib = load_library()
+    if start_event is None or stop_event is None:
+        lib.mla_decode_internal_set_kernel_events(None, None)
+    else:
+        lib.mla_decode_internal_set_kernel_events(start_event.cuda_event, stop_event.cuda_event)
 
 
 def fp8_to_bf16_device(codes):

@@ -653,6 +653,8 @@ __global__ void fp8_to_bf16_kernel(const u32x2* in, bf16x8* out, int64_t n) {
 constexpr int MAX_DEVICES = 64;
 std::atomic<int> g_cu_count[MAX_DEVICES];
 std::atomic<int> g_grid_override{0};
+std::atomic<void*> g_ev_start{nullptr};
+std::atomic<void*> g_ev_stop{nullptr};
 
 int device_grid(int* grid_out) {
   int dev = 0;
@@ -777,11 +779,15 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
 
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = dims->kv_dtype == MLA_KV_FP8_E4M3FN;
+  void* ev0 = g_ev_start.load(std::memory_order_relaxed);
+  void* ev1 = g_ev_stop.load(std::memory_order_relaxed);
+  if (ev0 != nullptr) (void)hipEventRecord((hipEvent_t)ev0, s);
   switch (dims->page_size) {
     case 16: fp8 ? launch_decode<true, 16>(p, s) : launch_decode<false, 16>(p, s); break;
     case 32: fp8 ? launch_decode<true, 32>(p, s) : launch_decode<false, 32>(p, s); break;
     default: fp8 ? launch_decode<true, 64>(p, s) : launch_decode<false, 64>(p, s); break;
   }
+  if (ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev1, s);
   const int items = dims->total_q * dims->num_heads;
   hipLaunchKernelGGL(mla_merge_kernel, dim3((items + 3) / 4), dim3(THREADS), 0, s, p);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
@@ -789,6 +795,11 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
 }
 
 void mla_decode_internal_set_grid_override(int32_t grid) { g_grid_override.store(grid > 0 ? grid : 0); }
+
+void mla_decode_internal_set_kernel_events(void* start_event, void* stop_event) {
+  g_ev_start.store(start_event);
+  g_ev_stop.store(stop_event);
+}
 
 int mla_decode_internal_fp8_to_bf16(const void* in, void* out, int64_t n_groups, void* stream) {
   if (!in || !out) return MLA_ERR_NULL_POINTER;
