@@ -43,21 +43,25 @@ namespace {
 
 constexpr int D_QK = 576;
 constexpr int D_V = 512;
-constexpr int TILE = 64;          // KV rows per LDS tile
+constexpr int TILE = 32;          // KV rows per LDS tile
+constexpr int NBUF = 3;           // tile buffers (prefetch distance 2)
 constexpr int THREADS = 256;      // 4 waves
 constexpr int PAIRS_WAVE = 32;   // (row, head) pairs per wave (MFMA N dimension)
 constexpr int PAIRS_BLOCK = 64;  // pairs per unit: 2 pair groups x 32
+constexpr int QK_STEPS = 18;     // 16-dim MFMA steps per wave: half of 576
 constexpr int ROWB_BF16 = D_QK * 2;            // 1152
 constexpr int ROWB_FP8 = D_QK;                 // 576
-constexpr int TILEB = TILE * ROWB_BF16;        // 73728 (fp8 tiles use half)
+constexpr int TILEB = TILE * ROWB_BF16;        // 36864 bytes per buffer (fp8 tiles use half)
 constexpr int PLAN_INTS = MLA_MAX_BATCH + 1;
-constexpr int XP_OFF = 2 * TILEB;                  // P exchange: [4 waves][2 chunks][64 lanes][16 B]
-constexpr int XM_OFF = XP_OFF + 4 * 2 * 64 * 16;   // max / sum exchange: [4 waves][32] floats
-constexpr int PLAN_OFF = XM_OFF + 4 * 32 * 4;
+constexpr int XS_OFF = NBUF * TILEB;           // partial-logit exchange: [4 waves][4][64 lanes][16 B]
+constexpr int XF_OFF = XS_OFF + 4 * 4096;      // restart flags: [2 parities][4 waves] ints
+constexpr int PLAN_OFF = XF_OFF + 2 * 4 * 4;
 constexpr int LDS_BYTES = PLAN_OFF + PLAN_INTS * 4;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float RESCALE_THRESHOLD = 8.0f;      // log2 units: P stays <= 256
+// The reference max is raised (restarting the segment) only when a logit beats
+// it by more than 2^32: P and the fp32 sums stay far from overflow below that.
+constexpr float RESCALE_THRESHOLD = 32.0f;
 
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 
@@ -67,6 +71,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
   const uint16_t* q;
@@ -117,6 +122,27 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_wave_base) 
                :
                : "v"(gptr), "s"(lds_wave_base)
                : "memory");
+}
+
+// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+// Both bases are wave-uniform; readfirstlane pins them to SGPRs even where the
+// call sits under a lane-divergent branch.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
+  const uint64_t sb = (uint64_t)(uintptr_t)sbase;
+  const uint64_t sbu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"((const void*)(uintptr_t)sbu), "s"(m0)
+               : "memory");
+}
+
+// Wave-uniform int32 load through the scalar cache (block-table entries).
+__device__ __forceinline__ int load_uniform_i32(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
 }
 
 template <int N>
@@ -177,9 +203,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 
 // ---------------------------------------------------------------- tile layout
 //
-// One LDS tile buffer holds 64 cache rows split in two blocks:
-//   bf16: latent block [64][1024 B] at 0, RoPE block [64][128 B] at 65536;
-//   fp8 : latent block [64][512 B]  at 0, RoPE block [64][64 B]  at 32768.
+// One LDS tile buffer holds 32 cache rows split in two blocks:
+//   bf16: latent block [32][1024 B] at 0, RoPE block [32][128 B] at 32768;
+//   fp8 : latent block [32][512 B]  at 0, RoPE block [32][64 B]  at 16384.
 // A latent row is then exactly one 64-lane x 16 B load.  16-byte chunks are
 // XOR-swizzled by row so the MFMA operand reads below are bank-conflict free:
 //   bf16: chunk ^ swz_bf16(row), 3 bits: the 8 rows of one A-read phase
@@ -233,62 +259,75 @@ __device__ void build_plan(const Params& p, int* tile_off, int* scan) {
 
 // ---------------------------------------------------------------- tile loader
 
+// DMA instructions one wave issues for a full tile.
+template <bool FP8>
+constexpr int tile_loads() { return FP8 ? 5 : 9; }
+
 // Start the loads of tile t of request b into the LDS buffer at byte offset buf.
-// Wave w fills rows [16w, 16w+16), which always sit in one page (page_size is a
+// Wave w fills rows [8w, 8w+8), which always sit in one page (page_size is a
 // multiple of 16), so the page base is wave-uniform.  Rows at or past seq_len are
 // never read from memory (nor is their block-table entry): they are zero-filled.
-// A full tile costs each wave exactly 18 (bf16) / 9 (fp8) DMA instructions.
+// A full tile costs each wave exactly tile_loads<FP8>() DMA instructions.
 template <bool FP8, int PS>
 __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t) {
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
-  const int row0 = t * TILE + 16 * w;
+  const int row0 = t * TILE + 8 * w;
   const uint32_t lds0 = lds_addr(smem);
   if (!FP8) {
-    const uint32_t lat = buf + 16 * w * 1024;
-    const uint32_t rope = buf + ROPE_OFF_BF16 + 16 * w * 128;
-    if (row0 >= L) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) lds_zero16(smem, lat + i * 1024 + lane * 16);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) lds_zero16(smem, rope + j * 1024 + lane * 16);
-      return;
-    }
-    const int page = uniform(p.block_tables[(size_t)b * p.bt_stride + row0 / PS]);
-    const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_BF16;
-    const int nvalid = L - row0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < nvalid) dma16(pg + i * ROWB_BF16 + ((lane ^ swz_bf16(i)) << 4), lds0 + lat + i * 1024);
-      else lds_zero16(smem, lat + i * 1024 + lane * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = 8 * j + (lane >> 3);
-      if (r < nvalid) dma16(pg + r * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_bf16(r)) << 4), lds0 + rope + j * 1024);
-      else lds_zero16(smem, rope + j * 1024 + lane * 16);
-    }
-  } else {
-    const uint32_t lat = buf + 16 * w * 512;
-    const uint32_t rope = buf + ROPE_OFF_FP8 + 16 * w * 64;
+    const uint32_t lat = buf + 8 * w * 1024;
+    const uint32_t rope = buf + ROPE_OFF_BF16 + 8 * w * 128;
     if (row0 >= L) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) lds_zero16(smem, lat + i * 1024 + lane * 16);
       lds_zero16(smem, rope + lane * 16);
       return;
     }
-    const int page = uniform(p.block_tables[(size_t)b * p.bt_stride + row0 / PS]);
-    const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_FP8;
+    const int page = load_uniform_i32(p.block_tables + (size_t)b * p.bt_stride + row0 / PS);
+    const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_BF16;
     const int nvalid = L - row0;
+    // the swizzle depends on the row's place in the tile (8w + i), not in the wave
+    const int rr = lane >> 3;  // RoPE: 8 lanes per row
+    const uint32_t rope_off = (uint32_t)(rr * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_bf16(8 * w + rr)) << 4));
+    if (nvalid >= 8) {
+      // all 8 rows live: scalar row base, 32-bit lane offset, no branches
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma16_s(pg + i * ROWB_BF16, (uint32_t)((lane ^ swz_bf16(8 * w + i)) << 4), lds0 + lat + i * 1024);
+      dma16_s(pg, rope_off, lds0 + rope);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = 2 * i + (lane >> 5);
-      if (r < nvalid) dma16(pg + r * ROWB_FP8 + (((lane & 31) ^ (r & 7)) << 4), lds0 + lat + i * 1024);
+      if (i < nvalid) dma16_s(pg + i * ROWB_BF16, (uint32_t)((lane ^ swz_bf16(8 * w + i)) << 4), lds0 + lat + i * 1024);
       else lds_zero16(smem, lat + i * 1024 + lane * 16);
     }
-    {
-      const int r = lane >> 2;
-      if (r < nvalid) dma16(pg + r * ROWB_FP8 + 512 + (((lane & 3) ^ (r & 3)) << 4), lds0 + rope);
+    if (rr < nvalid) dma16_s(pg, rope_off, lds0 + rope);
+    else lds_zero16(smem, rope + lane * 16);
+  } else {
+    const uint32_t lat = buf + 8 * w * 512;
+    const uint32_t rope = buf + ROPE_OFF_FP8 + 8 * w * 64;
+    if (row0 >= L) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_zero16(smem, lat + i * 1024 + lane * 16);
+      if (lane < 32) lds_zero16(smem, rope + lane * 16);
+      return;
+    }
+    const int page = load_uniform_i32(p.block_tables + (size_t)b * p.bt_stride + row0 / PS);
+    const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_FP8;
+    const int nvalid = L - row0;
+    const int hi = lane >> 5;
+    const int rr = lane >> 2;  // RoPE: 4 lanes per row, 32 lanes
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 2 * i + hi;
+      if (nvalid >= 8 || r < nvalid)
+        dma16_s(pg + 2 * i * ROWB_FP8, (uint32_t)(hi * ROWB_FP8 + (((lane & 31) ^ (r & 7)) << 4)),
+                lds0 + lat + i * 1024);
+      else lds_zero16(smem, lat + i * 1024 + lane * 16);
+    }
+    if (lane < 32) {
+      if (rr < nvalid) dma16_s(pg, (uint32_t)(rr * ROWB_FP8 + 512 + (((lane & 3) ^ (rr & 3)) << 4)), lds0 + rope);
       else lds_zero16(smem, rope + lane * 16);
     }
   }
@@ -298,15 +337,19 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 //
 // A unit is (request, block of 64 (row, head) pairs).  The four waves form two
 // pair groups of 32 pairs (grp = w >> 1) times two halves (hh = w & 1):
-//   * QK^T: wave (grp, hh) computes S^T for its 32 pairs over tokens
-//     [32hh, 32hh+32) of the tile (36 MFMAs, full 576-dim contraction);
-//   * the two halves swap their row maxima and their bf16 P through LDS, so
-//     both hold P for all 64 tokens of the tile;
+//   * QK^T: wave (grp, hh) contracts its 32 pairs against the tile over head
+//     dims [288hh, 288hh+288) (18 MFMAs) and the two halves add their fp32
+//     partial logits through LDS, so both hold the full S^T of the tile;
+//   * both run the same softmax, so both hold P for all 32 tokens;
 //   * P.V: wave (grp, hh) accumulates O^T for output dims [256hh, 256hh+256).
-// Each wave thus keeps Q (144 VGPRs) and half of O (128 accumulators).
+// Each wave keeps half of Q (72 VGPRs) and half of O (128 accumulators).
+// Returns false when the segment has to be redone: a logit beat its lane's
+// reference max by more than the threshold; m_seed then holds the raised
+// references and the caller runs the segment again (rare; O is never rescaled,
+// and the restart keeps the accumulators out of any loop-carried VALU path).
 template <bool FP8, int PS>
-__device__ __forceinline__ void process_segment(const Params& p, uint8_t* smem, int b, int pb, int L, int t0, int t1,
-                                                int slot) {
+__device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, int b, int pb, int L, int t0, int t1,
+                                                int slot, float& m_seed) {
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int grp = w >> 1;
@@ -324,30 +367,35 @@ __device__ __forceinline__ void process_segment(const Params& p, uint8_t* smem, 
   const int n_vis = !valid ? 0 : (p.causal ? L - qb + qi + 1 : L);
   const bool active = (pb * PAIRS_BLOCK + grp * PAIRS_WAVE) < npairs;  // uniform, same for both halves
 
-  // first tile in flight before the query loads
+  // first two tiles in flight before the query loads
   issue_tile<FP8, PS>(p, smem, 0, b, L, t0);
+  if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1);
 
-  // Query fragments: lane holds pair `col`, dims 16k + 8h .. +8 (B operand of QK^T).
-  bf16x8 qf[36];
+  // Query fragments: lane holds pair `col`, dims 16(18hh + k) + 8h .. +8 (B operand).
+  bf16x8 qf[QK_STEPS];
   {
-    const u32x4* qp = (const u32x4*)(p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 8 * h);
+    const u32x4* qp = (const u32x4*)(p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 288 * hh + 8 * h);
 #pragma unroll
-    for (int k = 0; k < 36; ++k) {
+    for (int k = 0; k < QK_STEPS; ++k) {
       const u32x4 v = (valid && active) ? qp[2 * k] : u32x4{0, 0, 0, 0};
       qf[k] = __builtin_bit_cast(bf16x8, v);
     }
+    // Consume the loads here so no wait on them is left inside the tile loop
+    // (where it would also wait for the next tiles' DMA).
+#pragma unroll
+    for (int k = 0; k < QK_STEPS; ++k) asm volatile("" : : "v"(qf[k]));
   }
 
   f32x16 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
-  float m_ref = -INFINITY;  // running reference max, log2 units (same in both halves)
+  float m_ref = m_seed;     // reference max, log2 units (identical in both halves)
   float lsum = 0.f;         // this lane's share of the softmax denominator
 
   // ---- lane-constant LDS offsets (see the tile layout above)
-  // QK^T A operand: logical row (lane & 31) of subtile hh is read from physical
-  // row prow; quartets 1 and 2 of each 16 rows are swapped so the MFMA result
-  // rows come out in the token order the P.V B operand needs.
+  // QK^T A operand: logical row (lane & 31) is read from physical row prow;
+  // quartets 1 and 2 of each 16 rows are swapped so the MFMA result rows come
+  // out in the token order the P.V B operand needs.
   const int lr = lane & 31;
   const int prow = (lr & 16) | (lr & 3) | ((lr & 4) << 1) | ((lr & 8) >> 1);
   const int s16 = lane & 15;
@@ -357,8 +405,8 @@ __device__ __forceinline__ void process_segment(const Params& p, uint8_t* smem, 
   if (!FP8) {
     const int sw = swz_bf16(prow);
     qsx = sw >> 1;
-    qa_lat = (32 * hh + prow) * 1024 + 16 * (h ^ (sw & 1));
-    qa_rope = ROPE_OFF_BF16 + (32 * hh + prow) * 128 + 16 * (h ^ (sw & 1));
+    qa_lat = prow * 1024 + 16 * (h ^ (sw & 1));
+    qa_rope = ROPE_OFF_BF16 + prow * 128 + 16 * (h ^ (sw & 1));
     // transposed read, this lane as source: token 8h + 4rd + sl of a 16-token
     // chunk, dims 32db + 16 g1 + 4 (s16 & 3) .. +4, db = 8hh + db'.
     const int sl = s16 >> 2;
@@ -371,48 +419,92 @@ __device__ __forceinline__ void process_segment(const Params& p, uint8_t* smem, 
     zz = 0;
   } else {
     qsx = prow & 7;
-    qa_lat = (32 * hh + prow) * 512 + 8 * h;
-    qa_rope = ROPE_OFF_FP8 + (32 * hh + prow) * 64 + 8 * h;
+    qa_lat = prow * 512 + 8 * h;
+    qa_rope = ROPE_OFF_FP8 + prow * 64 + 8 * h;
     // transposed read, this lane as source: token 8h + z, dims 32db + 16 g1 + 8 (s16 & 1) .. +8
     const int z = s16 >> 1;
     zz = z >> 1;
     tr8_base = (8 * h + z) * 512 + 16 * (g1 ^ (z & 1)) + 8 * (s16 & 1) + 256 * hh;
     tr_even = tr_odd = 0;
   }
-  const uint32_t xp_own = XP_OFF + (2 * w) * 1024 + lane * 16;
-  const uint32_t xp_other = XP_OFF + (2 * (w ^ 1)) * 1024 + lane * 16;
-  float* xm = (float*)(smem + XM_OFF);
+  const uint32_t xs_own = XS_OFF + w * 4096 + lane * 16;
+  const uint32_t xs_other = XS_OFF + (w ^ 1) * 4096 + lane * 16;
+  int* xflag = (int*)(smem + XF_OFF);
 
-  for (int t = t0; t < t1; ++t) {
-    const uint32_t cur = ((t - t0) & 1) ? TILEB : 0;
-    // Tile t is the only DMA in flight; after the barrier every wave has also
-    // finished tile t-1, so its buffer can take tile t+1.
-    wait_vmcnt<0>();
+  int t = t0;
+  for (;;) {
+    const int bi = (t - t0) % NBUF;
+    const uint32_t cur = bi * TILEB;
+    // In flight: tile t and tile t+1.  A full tile t+1 is exactly
+    // tile_loads() DMA ops; otherwise only a full drain proves tile t landed.
+    if (t + 1 < t1 && (t + 2) * TILE <= L) {
+      if (FP8) wait_vmcnt<tile_loads<true>()>(); else wait_vmcnt<tile_loads<false>()>();
+    } else {
+      wait_vmcnt<0>();
+    }
     wait_lgkm0();
     block_barrier();
-    if (t + 1 < t1) issue_tile<FP8, PS>(p, smem, cur ^ TILEB, b, L, t + 1);
+    // Every wave has finished tile t-1.  A wave whose logits beat its reference
+    // max by more than the threshold during tile t-1 asks for the segment to
+    // be redone from t0 with raised references.
+    if (t > t0 && uniform(xflag[((t - 1) & 1) * 4 + 0] | xflag[((t - 1) & 1) * 4 + 1] |
+                          xflag[((t - 1) & 1) * 4 + 2] | xflag[((t - 1) & 1) * 4 + 3]) != 0) {
+      wait_vmcnt<0>();
+      m_seed = m_ref;
+      return false;
+    }
+    if (t == t1) break;
+    if (t + 2 < t1) issue_tile<FP8, PS>(p, smem, ((bi + 2) % NBUF) * TILEB, b, L, t + 2);
 
     f32x16 s = f32x16{};
-    float mx = -INFINITY;
     if (active) {
-      // ---------------- S^T (32 tokens of half hh) = K . Q^T
-#pragma unroll
-      for (int k = 0; k < 36; ++k) {
-        bf16x8 a;
+      // ---------------- partial S^T (32 tokens) = K . Q^T over this wave's half of the dims
+      // A fragments are read GA steps ahead of their MFMA.
+      constexpr int GA = 4;
+      u32x4 araw[GA];
+      auto load_a = [&](int kk) -> u32x4 {
+        const int k = QK_STEPS * hh + kk;  // 16-dim step within 576 (runtime hh)
         if (FP8) {
           const uint32_t off = (k < 32) ? cur + qa_lat + (((k & 7) ^ qsx) << 4) + 128 * (k >> 3)
                                         : cur + qa_rope + (((k - 32) ^ (prow & 3)) << 4);
           const u32x2 raw = lds_read_b64(smem, off);
-          a = fp8x8_to_bf16x8(raw[0], raw[1]);
+          return u32x4{raw[0], raw[1], 0u, 0u};
         } else {
           const uint32_t off = (k < 32) ? cur + qa_lat + 32 * ((k & 3) ^ qsx) + 128 * (k >> 2)
                                         : cur + qa_rope + 32 * ((k - 32) ^ qsx);
-          a = __builtin_bit_cast(bf16x8, lds_read_b128(smem, off));
+          return lds_read_b128(smem, off);
         }
+      };
+#pragma unroll
+      for (int k = 0; k < GA; ++k) araw[k] = load_a(k);
+#pragma unroll
+      for (int k = 0; k < QK_STEPS; ++k) {
+        const u32x4 cur_raw = araw[k % GA];
+        if (k + GA < QK_STEPS) araw[k % GA] = load_a(k + GA);
+        const bf16x8 a = FP8 ? fp8x8_to_bf16x8(cur_raw[0], cur_raw[1]) : __builtin_bit_cast(bf16x8, cur_raw);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], s, 0, 0, 0);
       }
-      // value k is token 32hh + 16(k>>3) + 8h + (k&7) of the tile
-      const int tok0 = t * TILE + 32 * hh + 8 * h;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(__attribute__((address_space(3))) f32x4*)((__attribute__((address_space(3))) uint8_t*)smem + xs_own +
+                                                    j * 1024) = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+    }
+    wait_lgkm0();
+    block_barrier();
+    bool restart_me = false;
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(
+            (const __attribute__((address_space(3))) uint8_t*)smem + xs_other + j * 1024);
+        s[4 * j] += o[0];
+        s[4 * j + 1] += o[1];
+        s[4 * j + 2] += o[2];
+        s[4 * j + 3] += o[3];
+      }
+      // ---------------- softmax (exp2 domain); value k is token 16(k>>3) + 8h + (k&7)
+      const int tok0 = t * TILE + 8 * h;
+      float mx = -INFINITY;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         float v = s[k] * p.scale_log2;
@@ -421,74 +513,55 @@ __device__ __forceinline__ void process_segment(const Params& p, uint8_t* smem, 
         mx = fmaxf(mx, v);
       }
       mx = fmaxf(mx, other_half(mx));
-      if (h == 0) xm[w * 32 + col] = mx;
-    }
-    wait_lgkm0();
-    block_barrier();
-    if (active) {
-      mx = fmaxf(mx, xm[(w ^ 1) * 32 + col]);
-      // A lane with nothing accumulated adopts the tile max; one whose max grew
-      // by more than the threshold forces a (rare) rescale of O.
+      // A lane with nothing accumulated yet adopts the tile max as reference.
       if (m_ref == -INFINITY) m_ref = mx;
-      const bool grow = mx > m_ref + RESCALE_THRESHOLD;
-      if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
-        const float m_new = fmaxf(m_ref, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
-        m_ref = m_new;
-      }
+      restart_me = __builtin_amdgcn_ballot_w64(mx > m_ref + RESCALE_THRESHOLD) != 0;
+      if (restart_me) m_ref = fmaxf(m_ref, mx);
       const float mbase = (m_ref == -INFINITY) ? 0.f : m_ref;
+      bf16x8 pc[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        bf16x8 pc;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float e = __builtin_amdgcn_exp2f(s[8 * c + j] - mbase);
           lsum += e;
-          pc[j] = (__bf16)e;
-        }
-        *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + xp_own +
-                                                     c * 1024) = pc;
-      }
-    }
-    wait_lgkm0();
-    block_barrier();
-    if (active) {
-      // ---------------- O^T (dims of half hh) += V^T . P^T over the 4 chunks of 16 tokens
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // chunk c belongs to token half c >> 1; its P was written by wave (grp, c >> 1)
-        const uint32_t src = ((c >> 1) == hh ? xp_own : xp_other) + (c & 1) * 1024;
-        const bf16x8 pc =
-            *(const __attribute__((address_space(3))) bf16x8*)((const __attribute__((address_space(3))) uint8_t*)smem + src);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          bf16x8 vt;
-          if (FP8) {
-            const uint32_t off = cur + tr8_base + 32 * ((d & 3) ^ zz) + 128 * (d >> 2) + 16 * c * 512;
-            const i32x2 raw = lds_read_tr8(smem, off);
-            vt = fp8x8_to_bf16x8((uint32_t)raw[0], (uint32_t)raw[1]);
-          } else {
-            const uint32_t base = cur + ((d & 1) ? tr_odd : tr_even) + 64 * (d & ~1) + 16 * c * 1024;
-            const s16x4 lo = lds_read_tr16(smem, base);
-            const s16x4 hi = lds_read_tr16(smem, base + 4 * 1024);
-            vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pc, acc[d], 0, 0, 0);
+          pc[c][j] = (__bf16)e;
         }
       }
+      // ---------------- O^T (dims of half hh) += V^T . P^T over the 2 chunks of 16 tokens
+      // V^T fragments are read GV steps ahead of their MFMA (step = c * 8 + d).
+      constexpr int GV = 4;
+      u32x4 vraw[GV];
+      auto load_v = [&](int step) -> u32x4 {
+        const int c = step >> 3, d = step & 7;
+        if (FP8) {
+          const uint32_t off = cur + tr8_base + 32 * ((d & 3) ^ zz) + 128 * (d >> 2) + 16 * c * 512;
+          const i32x2 raw = lds_read_tr8(smem, off);
+          return u32x4{(uint32_t)raw[0], (uint32_t)raw[1], 0u, 0u};
+        } else {
+          const uint32_t base = cur + ((d & 1) ? tr_odd : tr_even) + 64 * (d & ~1) + 16 * c * 1024;
+          const s16x4 lo = lds_read_tr16(smem, base);
+          const s16x4 hi = lds_read_tr16(smem, base + 4 * 1024);
+          return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < GV; ++i) vraw[i] = load_v(i);
+#pragma unroll
+      for (int step = 0; step < 16; ++step) {
+        const u32x4 cur_raw = vraw[step % GV];
+        if (step + GV < 16) vraw[step % GV] = load_v(step + GV);
+        const bf16x8 vt = FP8 ? fp8x8_to_bf16x8(cur_raw[0], cur_raw[1]) : __builtin_bit_cast(bf16x8, cur_raw);
+        acc[step & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pc[step >> 3], acc[step & 7], 0, 0, 0);
+      }
     }
+    if (lane == 0) xflag[(t & 1) * 4 + w] = restart_me ? 1 : 0;
+    ++t;
   }
 
-  // ---------------- epilogue: combine the denominator over lane halves and token halves
+  // ---------------- epilogue: the two lane halves hold the two token halves
   lsum += other_half(lsum);
-  if (h == 0) xm[w * 32 + col] = lsum;
-  wait_lgkm0();
-  block_barrier();
-  lsum += xm[(w ^ 1) * 32 + col];
-  if (!active || !valid) return;
+  if (!active || !valid) return true;
   if (slot < 0) {
     const float inv = p.bmm2 / lsum;
     uint16_t* op = p.out + ((size_t)(r0 + qi) * H + head) * D_V + 256 * hh;
@@ -525,6 +598,7 @@ __device__ __forceinline__ void process_segment(const Params& p, uint8_t* smem, 
       ml[1] = lsum;
     }
   }
+  return true;
 }
 
 // ---------------------------------------------------------------- decode kernel
@@ -568,7 +642,9 @@ void mla_decode_kernel(Params p) {
     const int t1 = min(T, t0 + (end - x));
     const bool whole = (t0 == 0 && t1 == T);
     const int slot = whole ? -1 : (first ? 2 * g : 2 * g + 1);
-    process_segment<FP8, PS>(p, smem, b, pb, L, t0, t1, slot);
+    float m_seed = -INFINITY;
+    while (!process_segment<FP8, PS>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
+    }
     x += t1 - t0;
     first = false;
   }
