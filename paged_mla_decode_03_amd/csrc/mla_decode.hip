@@ -44,7 +44,7 @@ namespace {
 constexpr int D_QK = 576;
 constexpr int D_V = 512;
 constexpr int TILE = 32;          // KV rows per LDS tile
-constexpr int NBUF = 3;           // tile buffers (prefetch distance 2)
+constexpr int NBUF = 4;           // tile buffers: tiles t..t+2 resident or landing, t+3 being issued
 constexpr int THREADS = 256;      // 4 waves
 constexpr int PAIRS_WAVE = 32;   // (row, head) pairs per wave (MFMA N dimension)
 constexpr int PAIRS_BLOCK = 64;  // pairs per unit: 2 pair groups x 32
@@ -54,13 +54,15 @@ constexpr int ROWB_FP8 = D_QK;                 // 576
 constexpr int TILEB = TILE * ROWB_BF16;        // 36864 bytes per buffer (fp8 tiles use half)
 constexpr int PLAN_INTS = MLA_MAX_BATCH + 1;
 constexpr int XS_OFF = NBUF * TILEB;           // partial-logit exchange: [4 waves][4][64 lanes][16 B]
-constexpr int XF_OFF = XS_OFF + 4 * 4096;      // restart flags: [2 parities][4 waves] ints
-constexpr int PLAN_OFF = XF_OFF + 2 * 4 * 4;
-constexpr int LDS_BYTES = PLAN_OFF + PLAN_INTS * 4;
+constexpr int LDS_BYTES = XS_OFF + 4 * 4096;   // 163840: the whole LDS of a CU
+// The work-plan scan (prologue only) and the end-of-segment flags alias the
+// tile buffers / the exchange area when those are idle.
+constexpr int PLAN_SCRATCH_OFF = 0;
+constexpr int SCAN_SCRATCH_OFF = PLAN_INTS * 4 + 60;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-// The reference max is raised (restarting the segment) only when a logit beats
-// it by more than 2^32: P and the fp32 sums stay far from overflow below that.
+// A segment is redone with a raised reference max only when a logit beats the
+// reference by more than 2^32: P and the fp32 sums stay far from overflow below.
 constexpr float RESCALE_THRESHOLD = 32.0f;
 
 static_assert(LDS_BYTES <= 163840, "LDS budget");
@@ -206,16 +208,22 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // One LDS tile buffer holds 32 cache rows split in two blocks:
 //   bf16: latent block [32][1024 B] at 0, RoPE block [32][128 B] at 32768;
 //   fp8 : latent block [32][512 B]  at 0, RoPE block [32][64 B]  at 16384.
-// A latent row is then exactly one 64-lane x 16 B load.  16-byte chunks are
-// XOR-swizzled by row so the MFMA operand reads below are bank-conflict free:
-//   bf16: chunk ^ swz_bf16(row), 3 bits: the 8 rows of one A-read phase
-//         ({0..3, 8..11} after the row permutation) and the 4 rows of one
-//         transposed read land on 8 distinct chunks.
-//   fp8 : latent chunk ^ (row & 7), RoPE chunk ^ (row & 3).
+// A latent row is then one 64-lane x 16 B load (bf16) or half of one (fp8).
+// 16-byte chunks are XOR-swizzled by row so that both operand reads are
+// bank-conflict free (64 banks x 4 B):
+//   * the QK^T A read: 16 lanes read the same chunk of 16 different rows;
+//   * the transposed V^T read: one instruction touches 8 rows x 64 B.
+//   bf16 latent: chunk ^ (((row & 3) << 2) | ((row >> 2) & 3))   (4 bits)
+//   bf16 RoPE  : chunk ^ ((row >> 1) & 7)                         (3 bits)
+//   fp8 latent : chunk ^ (row & 15)                               (4 bits)
+//   fp8 RoPE   : chunk ^ ((row >> 2) & 3)                         (2 bits)
 constexpr int ROPE_OFF_BF16 = TILE * 1024;
 constexpr int ROPE_OFF_FP8 = TILE * 512;
 
-__device__ __forceinline__ constexpr int swz_bf16(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ constexpr int swz_lat_bf16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ constexpr int swz_rope_bf16(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ constexpr int swz_lat_fp8(int row) { return row & 15; }
+__device__ __forceinline__ constexpr int swz_rope_fp8(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ void lds_zero16(uint8_t* smem, uint32_t off) {
   *(__attribute__((address_space(3))) u32x4*)((__attribute__((address_space(3))) uint8_t*)smem + off) =
@@ -286,20 +294,21 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
     const int page = load_uniform_i32(p.block_tables + (size_t)b * p.bt_stride + row0 / PS);
     const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_BF16;
     const int nvalid = L - row0;
-    // the swizzle depends on the row's place in the tile (8w + i), not in the wave
+    // swizzles use the row's place in the tile (8w + i)
     const int rr = lane >> 3;  // RoPE: 8 lanes per row
-    const uint32_t rope_off = (uint32_t)(rr * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_bf16(8 * w + rr)) << 4));
+    const uint32_t rope_off = (uint32_t)(rr * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_rope_bf16(8 * w + rr)) << 4));
     if (nvalid >= 8) {
       // all 8 rows live: scalar row base, 32-bit lane offset, no branches
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        dma16_s(pg + i * ROWB_BF16, (uint32_t)((lane ^ swz_bf16(8 * w + i)) << 4), lds0 + lat + i * 1024);
+        dma16_s(pg + i * ROWB_BF16, (uint32_t)((lane ^ swz_lat_bf16(8 * w + i)) << 4), lds0 + lat + i * 1024);
       dma16_s(pg, rope_off, lds0 + rope);
       return;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i < nvalid) dma16_s(pg + i * ROWB_BF16, (uint32_t)((lane ^ swz_bf16(8 * w + i)) << 4), lds0 + lat + i * 1024);
+      if (i < nvalid)
+        dma16_s(pg + i * ROWB_BF16, (uint32_t)((lane ^ swz_lat_bf16(8 * w + i)) << 4), lds0 + lat + i * 1024);
       else lds_zero16(smem, lat + i * 1024 + lane * 16);
     }
     if (rr < nvalid) dma16_s(pg, rope_off, lds0 + rope);
@@ -322,12 +331,13 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
     for (int i = 0; i < 4; ++i) {
       const int r = 2 * i + hi;
       if (nvalid >= 8 || r < nvalid)
-        dma16_s(pg + 2 * i * ROWB_FP8, (uint32_t)(hi * ROWB_FP8 + (((lane & 31) ^ (r & 7)) << 4)),
+        dma16_s(pg + 2 * i * ROWB_FP8, (uint32_t)(hi * ROWB_FP8 + (((lane & 31) ^ swz_lat_fp8(8 * w + r)) << 4)),
                 lds0 + lat + i * 1024);
       else lds_zero16(smem, lat + i * 1024 + lane * 16);
     }
     if (lane < 32) {
-      if (rr < nvalid) dma16_s(pg, (uint32_t)(rr * ROWB_FP8 + 512 + (((lane & 3) ^ (rr & 3)) << 4)), lds0 + rope);
+      if (rr < nvalid)
+        dma16_s(pg, (uint32_t)(rr * ROWB_FP8 + 512 + (((lane & 3) ^ swz_rope_fp8(8 * w + rr)) << 4)), lds0 + rope);
       else lds_zero16(smem, rope + lane * 16);
     }
   }
@@ -337,16 +347,217 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 //
 // A unit is (request, block of 64 (row, head) pairs).  The four waves form two
 // pair groups of 32 pairs (grp = w >> 1) times two halves (hh = w & 1):
-//   * QK^T: wave (grp, hh) contracts its 32 pairs against the tile over head
-//     dims [288hh, 288hh+288) (18 MFMAs) and the two halves add their fp32
+//   * QK^T: wave (grp, hh) contracts its 32 pairs against a tile over half of
+//     the 576 head dims -- latent dims [256hh, 256hh+256) and RoPE dims
+//     [512+32hh, 512+32hh+32) -- in 18 MFMAs; the two halves add their fp32
 //     partial logits through LDS, so both hold the full S^T of the tile;
 //   * both run the same softmax, so both hold P for all 32 tokens;
 //   * P.V: wave (grp, hh) accumulates O^T for output dims [256hh, 256hh+256).
 // Each wave keeps half of Q (72 VGPRs) and half of O (128 accumulators).
-// Returns false when the segment has to be redone: a logit beat its lane's
-// reference max by more than the threshold; m_seed then holds the raised
-// references and the caller runs the segment again (rare; O is never rescaled,
-// and the restart keeps the accumulators out of any loop-carried VALU path).
+//
+// Software pipeline over tiles (4 LDS buffers), iteration t:
+//   barrier A  -> tile t+1 is in LDS, tile t-1's buffer is free: issue tile t+3;
+//                 read the partner's partial logits of tile t
+//   softmax(t) alongside QK^T(t+1) on the matrix cores
+//   barrier B  -> the partner has read this wave's exchange slot
+//   write the partial logits of tile t+1; P.V(t)
+// Waves whose pair group is empty run the same barrier and DMA sequence only.
+
+// Per-lane state of an active wave.
+struct SegState {
+  f32x16 acc[8];   // O^T accumulators
+  float m_ref;     // reference max, log2 units (identical in both halves)
+  float m_max;     // largest logit seen, log2 units
+  float lsum;      // this lane's share of the softmax denominator
+  bool over;       // some logit beat m_ref by more than the threshold
+};
+
+template <bool FP8, int PS, bool ACTIVE>
+__device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int b, int L, int t0, int t1,
+                                             const bf16x8 (&qf)[QK_STEPS], int n_vis, SegState& st) {
+  constexpr int LOADS = tile_loads<FP8>();
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int hh = w & 1;
+  const int h = lane >> 5;
+  auto buf_of = [&](int t) -> uint32_t { return (uint32_t)((t - t0) % NBUF) * TILEB; };
+
+  // ---- lane-constant LDS offsets (see the tile layout above)
+  // QK^T A operand: logical row (lane & 31) is read from physical row prow;
+  // quartets 1 and 2 of each 16 rows are swapped so the MFMA result rows come
+  // out in the token order the P.V B operand needs.
+  const int lr = lane & 31;
+  const int prow = (lr & 16) | (lr & 3) | ((lr & 4) << 1) | ((lr & 8) >> 1);
+  const int s16 = lane & 15;
+  const int g1 = (lane >> 4) & 1;
+  uint32_t qa_lat, qa_rope0, qa_rope1, tr_base;
+  int qs_lat, tr_sl, tr_cc, tr_z;
+  if (!FP8) {
+    const int sl = swz_lat_bf16(prow), sr = swz_rope_bf16(prow);
+    qa_lat = prow * 1024 + 512 * hh + 16 * (h ^ (sl & 1));
+    qs_lat = sl >> 1;
+    qa_rope0 = ROPE_OFF_BF16 + prow * 128 + 16 * ((4 * hh + h) ^ sr);
+    qa_rope1 = ROPE_OFF_BF16 + prow * 128 + 16 * ((4 * hh + 2 + h) ^ sr);
+    tr_sl = s16 >> 2;
+    tr_cc = 2 * g1 + ((s16 & 3) >> 1);
+    tr_base = (8 * h + tr_sl) * 1024 + 512 * hh + 8 * (s16 & 1);
+    tr_z = 0;
+  } else {
+    qa_lat = prow * 512 + 256 * hh + 8 * h;
+    qs_lat = swz_lat_fp8(prow);
+    const int sr = swz_rope_fp8(prow);
+    qa_rope0 = ROPE_OFF_FP8 + prow * 64 + 16 * ((2 * hh) ^ sr) + 8 * h;
+    qa_rope1 = ROPE_OFF_FP8 + prow * 64 + 16 * ((2 * hh + 1) ^ sr) + 8 * h;
+    tr_z = s16 >> 1;
+    tr_base = (8 * h + tr_z) * 512 + 256 * hh + 8 * (s16 & 1);
+    tr_sl = tr_cc = 0;
+  }
+  const uint32_t xs_own = XS_OFF + w * 4096 + lane * 16;
+  const uint32_t xs_other = XS_OFF + (w ^ 1) * 4096 + lane * 16;
+
+  // A fragment for 16-dim step kk of this wave (0..15 latent, 16..17 RoPE)
+  auto load_a = [&](uint32_t buf, int kk) -> u32x4 {
+    if (FP8) {
+      const uint32_t off = (kk < 16) ? buf + qa_lat + 16 * (kk ^ qs_lat) : buf + (kk == 16 ? qa_rope0 : qa_rope1);
+      const u32x2 raw = lds_read_b64(smem, off);
+      return u32x4{raw[0], raw[1], 0u, 0u};
+    } else {
+      const uint32_t off = (kk < 16) ? buf + qa_lat + 256 * (kk >> 3) + 32 * ((kk & 7) ^ qs_lat)
+                                     : buf + (kk == 16 ? qa_rope0 : qa_rope1);
+      return lds_read_b128(smem, off);
+    }
+  };
+  // V^T fragment for step = c * 8 + d (chunk c of 16 tokens, dim block d of 32)
+  auto load_v = [&](uint32_t buf, int step) -> u32x4 {
+    const int c = step >> 3, d = step & 7;
+    if (FP8) {
+      const uint32_t off = buf + 16 * c * 512 + tr_base + 16 * ((2 * d + g1) ^ (8 * h + tr_z));
+      const i32x2 raw = lds_read_tr8(smem, off);
+      return u32x4{(uint32_t)raw[0], (uint32_t)raw[1], 0u, 0u};
+    } else {
+      const uint32_t off = buf + 16 * c * 1024 + tr_base + 64 * (d & 4) + 64 * ((d & 3) ^ tr_sl);
+      const s16x4 lo = lds_read_tr16(smem, off + 16 * (tr_cc ^ (2 * h)));
+      const s16x4 hi = lds_read_tr16(smem, off + 4 * 1024 + 16 * (tr_cc ^ (2 * h + 1)));
+      return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto to_bf16 = [&](const u32x4& raw) -> bf16x8 {
+    return FP8 ? fp8x8_to_bf16x8(raw[0], raw[1]) : __builtin_bit_cast(bf16x8, raw);
+  };
+  auto qk_partial = [&](uint32_t buf) -> f32x16 {
+    f32x16 s = f32x16{};
+    constexpr int GA = 4;  // A fragments read this many steps ahead
+    u32x4 araw[GA];
+#pragma unroll
+    for (int k = 0; k < GA; ++k) araw[k] = load_a(buf, k);
+#pragma unroll
+    for (int k = 0; k < QK_STEPS; ++k) {
+      const u32x4 cur = araw[k % GA];
+      if (k + GA < QK_STEPS) araw[k % GA] = load_a(buf, k + GA);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to_bf16(cur), qf[k], s, 0, 0, 0);
+    }
+    return s;
+  };
+  auto store_partial = [&](const f32x16& v) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(__attribute__((address_space(3))) f32x4*)((__attribute__((address_space(3))) uint8_t*)smem + xs_own +
+                                                  j * 1024) = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+  };
+
+  // Tile t has landed once at most the DMA ops of the n tiles issued after it
+  // remain; a partial tile among them makes the count unknown, so drain.
+  auto wait_tile = [&](int t, int n) {
+    n = min(n, t1 - 1 - t);
+    if (n <= 0 || (t + n + 1) * TILE > L) wait_vmcnt<0>();
+    else if (n == 1) wait_vmcnt<LOADS>();
+    else wait_vmcnt<2 * LOADS>();
+  };
+
+  // ---- prologue: partial logits of tile t0
+  wait_tile(t0, 2);
+  wait_lgkm0();
+  block_barrier();
+  f32x16 sp = f32x16{};
+  if (ACTIVE) {
+    sp = qk_partial(buf_of(t0));
+    store_partial(sp);
+  }
+
+  for (int t = t0; t < t1; ++t) {
+    if (t + 1 < t1) wait_tile(t + 1, 1);
+    wait_lgkm0();
+    block_barrier();  // A
+    if (t + 3 < t1) issue_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3);
+    if (!ACTIVE) {
+      wait_lgkm0();
+      block_barrier();  // B
+      continue;
+    }
+    // full logits of tile t: own partial + partner's
+    f32x16 s = sp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(
+          (const __attribute__((address_space(3))) uint8_t*)smem + xs_other + j * 1024);
+      s[4 * j] += o[0];
+      s[4 * j + 1] += o[1];
+      s[4 * j + 2] += o[2];
+      s[4 * j + 3] += o[3];
+    }
+    // QK^T of the next tile (past the last tile the buffer holds stale rows;
+    // the result is then unused) runs on the matrix cores under the softmax.
+    const f32x16 sn = qk_partial(buf_of(t + 1));
+    // ---------------- softmax (exp2 domain); value k is token 16(k>>3) + 8h + (k&7)
+    const int tok0 = t * TILE + 8 * h;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float v = s[k] * p.scale_log2;
+      v = (tok0 + 16 * (k >> 3) + (k & 7)) < n_vis ? v : -INFINITY;
+      s[k] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, other_half(mx));
+    if (st.m_ref == -INFINITY) st.m_ref = mx;  // first visible tile sets the reference
+    st.m_max = fmaxf(st.m_max, mx);
+    st.over = st.over || (mx > st.m_ref + RESCALE_THRESHOLD);
+    const float mbase = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+    bf16x8 pc0, pc1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e0 = __builtin_amdgcn_exp2f(s[j] - mbase);
+      const float e1 = __builtin_amdgcn_exp2f(s[8 + j] - mbase);
+      st.lsum += e0 + e1;
+      pc0[j] = (__bf16)e0;
+      pc1[j] = (__bf16)e1;
+    }
+    wait_lgkm0();
+    block_barrier();  // B
+    store_partial(sn);
+    // ---------------- O^T (this wave's 256 dims) += V^T . P^T over the two 16-token chunks
+    {
+      const uint32_t buf = buf_of(t);
+      constexpr int GV = 4;  // V^T fragments read this many steps ahead
+      u32x4 vraw[GV];
+#pragma unroll
+      for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
+#pragma unroll
+      for (int step = 0; step < 16; ++step) {
+        const u32x4 cur = vraw[step % GV];
+        if (step + GV < 16) vraw[step % GV] = load_v(buf, step + GV);
+        st.acc[step & 7] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(to_bf16(cur), (step >> 3) ? pc1 : pc0, st.acc[step & 7], 0, 0, 0);
+      }
+    }
+    sp = sn;
+  }
+}
+
+// Returns false when the segment has to be redone: some logit beat its lane's
+// reference max (the first visible tile's max) by more than 2^32.  m_seed then
+// holds each lane's observed max as the new reference and the caller runs the
+// segment again, which cannot overflow; O is never rescaled.
 template <bool FP8, int PS>
 __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, int b, int pb, int L, int t0, int t1,
                                                 int slot, float& m_seed) {
@@ -367,200 +578,52 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   const int n_vis = !valid ? 0 : (p.causal ? L - qb + qi + 1 : L);
   const bool active = (pb * PAIRS_BLOCK + grp * PAIRS_WAVE) < npairs;  // uniform, same for both halves
 
-  // first two tiles in flight before the query loads
+  // first three tiles in flight before the query loads
   issue_tile<FP8, PS>(p, smem, 0, b, L, t0);
   if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1);
+  if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2);
 
-  // Query fragments: lane holds pair `col`, dims 16(18hh + k) + 8h .. +8 (B operand).
+  // Query fragments (B operand): lane holds pair `col`; step kk < 16 covers latent
+  // dims 256hh + 16kk + 8h .. +8, steps 16, 17 RoPE dims 512 + 32hh + 16(kk-16) + 8h.
   bf16x8 qf[QK_STEPS];
   {
-    const u32x4* qp = (const u32x4*)(p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 288 * hh + 8 * h);
+    const uint16_t* qrow = p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 8 * h;
 #pragma unroll
     for (int k = 0; k < QK_STEPS; ++k) {
-      const u32x4 v = (valid && active) ? qp[2 * k] : u32x4{0, 0, 0, 0};
+      const int dim = k < 16 ? 256 * hh + 16 * k : 512 + 32 * hh + 16 * (k - 16);
+      const u32x4 v = (valid && active) ? *(const u32x4*)(qrow + dim) : u32x4{0, 0, 0, 0};
       qf[k] = __builtin_bit_cast(bf16x8, v);
     }
     // Consume the loads here so no wait on them is left inside the tile loop
-    // (where it would also wait for the next tiles' DMA).
+    // (where it would also wait for the tiles' DMA).
 #pragma unroll
     for (int k = 0; k < QK_STEPS; ++k) asm volatile("" : : "v"(qf[k]));
   }
 
-  f32x16 acc[8];
+  SegState st;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
-  float m_ref = m_seed;     // reference max, log2 units (identical in both halves)
-  float lsum = 0.f;         // this lane's share of the softmax denominator
+  for (int i = 0; i < 8; ++i) st.acc[i] = f32x16{};
+  st.m_ref = m_seed;
+  st.m_max = m_seed;
+  st.lsum = 0.f;
+  st.over = false;
+  if (active) segment_loop<FP8, PS, true>(p, smem, b, L, t0, t1, qf, n_vis, st);
+  else segment_loop<FP8, PS, false>(p, smem, b, L, t0, t1, qf, n_vis, st);
 
-  // ---- lane-constant LDS offsets (see the tile layout above)
-  // QK^T A operand: logical row (lane & 31) is read from physical row prow;
-  // quartets 1 and 2 of each 16 rows are swapped so the MFMA result rows come
-  // out in the token order the P.V B operand needs.
-  const int lr = lane & 31;
-  const int prow = (lr & 16) | (lr & 3) | ((lr & 4) << 1) | ((lr & 8) >> 1);
-  const int s16 = lane & 15;
-  const int g1 = (lane >> 4) & 1;
-  uint32_t qa_lat, qa_rope, tr_even, tr_odd, tr8_base;
-  int qsx, zz;
-  if (!FP8) {
-    const int sw = swz_bf16(prow);
-    qsx = sw >> 1;
-    qa_lat = prow * 1024 + 16 * (h ^ (sw & 1));
-    qa_rope = ROPE_OFF_BF16 + prow * 128 + 16 * (h ^ (sw & 1));
-    // transposed read, this lane as source: token 8h + 4rd + sl of a 16-token
-    // chunk, dims 32db + 16 g1 + 4 (s16 & 3) .. +4, db = 8hh + db'.
-    const int sl = s16 >> 2;
-    const int x = (2 * g1 + ((s16 & 3) >> 1)) ^ ((sl << 1) | h);
-    const int xb = x >> 2;
-    const uint32_t tl = (8 * h + sl) * 1024 + (x & 3) * 16 + 8 * (s16 & 1) + 512 * hh;
-    tr_even = tl + 64 * xb;
-    tr_odd = tl + 64 * (1 - xb);
-    tr8_base = 0;
-    zz = 0;
-  } else {
-    qsx = prow & 7;
-    qa_lat = prow * 512 + 8 * h;
-    qa_rope = ROPE_OFF_FP8 + prow * 64 + 8 * h;
-    // transposed read, this lane as source: token 8h + z, dims 32db + 16 g1 + 8 (s16 & 1) .. +8
-    const int z = s16 >> 1;
-    zz = z >> 1;
-    tr8_base = (8 * h + z) * 512 + 16 * (g1 ^ (z & 1)) + 8 * (s16 & 1) + 256 * hh;
-    tr_even = tr_odd = 0;
-  }
-  const uint32_t xs_own = XS_OFF + w * 4096 + lane * 16;
-  const uint32_t xs_other = XS_OFF + (w ^ 1) * 4096 + lane * 16;
-  int* xflag = (int*)(smem + XF_OFF);
-
-  int t = t0;
-  for (;;) {
-    const int bi = (t - t0) % NBUF;
-    const uint32_t cur = bi * TILEB;
-    // In flight: tile t and tile t+1.  A full tile t+1 is exactly
-    // tile_loads() DMA ops; otherwise only a full drain proves tile t landed.
-    if (t + 1 < t1 && (t + 2) * TILE <= L) {
-      if (FP8) wait_vmcnt<tile_loads<true>()>(); else wait_vmcnt<tile_loads<false>()>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    wait_lgkm0();
-    block_barrier();
-    // Every wave has finished tile t-1.  A wave whose logits beat its reference
-    // max by more than the threshold during tile t-1 asks for the segment to
-    // be redone from t0 with raised references.
-    if (t > t0 && uniform(xflag[((t - 1) & 1) * 4 + 0] | xflag[((t - 1) & 1) * 4 + 1] |
-                          xflag[((t - 1) & 1) * 4 + 2] | xflag[((t - 1) & 1) * 4 + 3]) != 0) {
-      wait_vmcnt<0>();
-      m_seed = m_ref;
-      return false;
-    }
-    if (t == t1) break;
-    if (t + 2 < t1) issue_tile<FP8, PS>(p, smem, ((bi + 2) % NBUF) * TILEB, b, L, t + 2);
-
-    f32x16 s = f32x16{};
-    if (active) {
-      // ---------------- partial S^T (32 tokens) = K . Q^T over this wave's half of the dims
-      // A fragments are read GA steps ahead of their MFMA.
-      constexpr int GA = 4;
-      u32x4 araw[GA];
-      auto load_a = [&](int kk) -> u32x4 {
-        const int k = QK_STEPS * hh + kk;  // 16-dim step within 576 (runtime hh)
-        if (FP8) {
-          const uint32_t off = (k < 32) ? cur + qa_lat + (((k & 7) ^ qsx) << 4) + 128 * (k >> 3)
-                                        : cur + qa_rope + (((k - 32) ^ (prow & 3)) << 4);
-          const u32x2 raw = lds_read_b64(smem, off);
-          return u32x4{raw[0], raw[1], 0u, 0u};
-        } else {
-          const uint32_t off = (k < 32) ? cur + qa_lat + 32 * ((k & 3) ^ qsx) + 128 * (k >> 2)
-                                        : cur + qa_rope + 32 * ((k - 32) ^ qsx);
-          return lds_read_b128(smem, off);
-        }
-      };
-#pragma unroll
-      for (int k = 0; k < GA; ++k) araw[k] = load_a(k);
-#pragma unroll
-      for (int k = 0; k < QK_STEPS; ++k) {
-        const u32x4 cur_raw = araw[k % GA];
-        if (k + GA < QK_STEPS) araw[k % GA] = load_a(k + GA);
-        const bf16x8 a = FP8 ? fp8x8_to_bf16x8(cur_raw[0], cur_raw[1]) : __builtin_bit_cast(bf16x8, cur_raw);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], s, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *(__attribute__((address_space(3))) f32x4*)((__attribute__((address_space(3))) uint8_t*)smem + xs_own +
-                                                    j * 1024) = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
-    }
-    wait_lgkm0();
-    block_barrier();
-    bool restart_me = false;
-    if (active) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(
-            (const __attribute__((address_space(3))) uint8_t*)smem + xs_other + j * 1024);
-        s[4 * j] += o[0];
-        s[4 * j + 1] += o[1];
-        s[4 * j + 2] += o[2];
-        s[4 * j + 3] += o[3];
-      }
-      // ---------------- softmax (exp2 domain); value k is token 16(k>>3) + 8h + (k&7)
-      const int tok0 = t * TILE + 8 * h;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        float v = s[k] * p.scale_log2;
-        v = (tok0 + 16 * (k >> 3) + (k & 7)) < n_vis ? v : -INFINITY;
-        s[k] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = fmaxf(mx, other_half(mx));
-      // A lane with nothing accumulated yet adopts the tile max as reference.
-      if (m_ref == -INFINITY) m_ref = mx;
-      restart_me = __builtin_amdgcn_ballot_w64(mx > m_ref + RESCALE_THRESHOLD) != 0;
-      if (restart_me) m_ref = fmaxf(m_ref, mx);
-      const float mbase = (m_ref == -INFINITY) ? 0.f : m_ref;
-      bf16x8 pc[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e = __builtin_amdgcn_exp2f(s[8 * c + j] - mbase);
-          lsum += e;
-          pc[c][j] = (__bf16)e;
-        }
-      }
-      // ---------------- O^T (dims of half hh) += V^T . P^T over the 2 chunks of 16 tokens
-      // V^T fragments are read GV steps ahead of their MFMA (step = c * 8 + d).
-      constexpr int GV = 4;
-      u32x4 vraw[GV];
-      auto load_v = [&](int step) -> u32x4 {
-        const int c = step >> 3, d = step & 7;
-        if (FP8) {
-          const uint32_t off = cur + tr8_base + 32 * ((d & 3) ^ zz) + 128 * (d >> 2) + 16 * c * 512;
-          const i32x2 raw = lds_read_tr8(smem, off);
-          return u32x4{(uint32_t)raw[0], (uint32_t)raw[1], 0u, 0u};
-        } else {
-          const uint32_t base = cur + ((d & 1) ? tr_odd : tr_even) + 64 * (d & ~1) + 16 * c * 1024;
-          const s16x4 lo = lds_read_tr16(smem, base);
-          const s16x4 hi = lds_read_tr16(smem, base + 4 * 1024);
-          return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-      };
-#pragma unroll
-      for (int i = 0; i < GV; ++i) vraw[i] = load_v(i);
-#pragma unroll
-      for (int step = 0; step < 16; ++step) {
-        const u32x4 cur_raw = vraw[step % GV];
-        if (step + GV < 16) vraw[step % GV] = load_v(step + GV);
-        const bf16x8 vt = FP8 ? fp8x8_to_bf16x8(cur_raw[0], cur_raw[1]) : __builtin_bit_cast(bf16x8, cur_raw);
-        acc[step & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pc[step >> 3], acc[step & 7], 0, 0, 0);
-      }
-    }
-    if (lane == 0) xflag[(t & 1) * 4 + w] = restart_me ? 1 : 0;
-    ++t;
+  // ---- segment end: all waves idle on LDS; one flag per wave says "redo"
+  int* flags = (int*)(smem + XS_OFF);
+  wait_lgkm0();
+  block_barrier();
+  if (lane == 0) flags[w] = __builtin_amdgcn_ballot_w64(st.over) != 0 ? 1 : 0;
+  wait_lgkm0();
+  block_barrier();
+  if (uniform(flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
+    m_seed = st.m_max;
+    return false;
   }
 
   // ---------------- epilogue: the two lane halves hold the two token halves
-  lsum += other_half(lsum);
+  float lsum = st.lsum + other_half(st.lsum);
   if (!active || !valid) return true;
   if (slot < 0) {
     const float inv = p.bmm2 / lsum;
@@ -573,14 +636,14 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
         u32x2 packed;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const __bf16 lo = (__bf16)(acc[d][4 * q4 + 2 * e] * inv);
-          const __bf16 hi = (__bf16)(acc[d][4 * q4 + 2 * e + 1] * inv);
+          const __bf16 lo = (__bf16)(st.acc[d][4 * q4 + 2 * e] * inv);
+          const __bf16 hi = (__bf16)(st.acc[d][4 * q4 + 2 * e + 1] * inv);
           packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
         }
         *(u32x2*)(op + dim) = packed;
       }
     }
-    if (p.lse != nullptr && h == 0 && hh == 0) p.lse[(size_t)(r0 + qi) * H + head] = (m_ref + __log2f(lsum)) * LN2;
+    if (p.lse != nullptr && h == 0 && hh == 0) p.lse[(size_t)(r0 + qi) * H + head] = (st.m_ref + __log2f(lsum)) * LN2;
   } else {
     const int pl = grp * PAIRS_WAVE + col;
     float* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V + 256 * hh;
@@ -589,12 +652,13 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int dim = 32 * d + 8 * q4 + 4 * h;
-        *(float4*)(wo + dim) = make_float4(acc[d][4 * q4], acc[d][4 * q4 + 1], acc[d][4 * q4 + 2], acc[d][4 * q4 + 3]);
+        *(float4*)(wo + dim) =
+            make_float4(st.acc[d][4 * q4], st.acc[d][4 * q4 + 1], st.acc[d][4 * q4 + 2], st.acc[d][4 * q4 + 3]);
       }
     }
     if (h == 0 && hh == 0) {
       float* ml = p.ws_ml + ((size_t)slot * PAIRS_BLOCK + pl) * 2;
-      ml[0] = m_ref;
+      ml[0] = st.m_ref;
       ml[1] = lsum;
     }
   }
@@ -607,8 +671,9 @@ template <bool FP8, int PS>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-  int* tile_off = (int*)(smem + PLAN_OFF);
-  build_plan(p, tile_off, (int*)smem);
+  // The plan lives in LDS only until this workgroup has found its starting point.
+  int* tile_off = (int*)(smem + PLAN_SCRATCH_OFF);
+  build_plan(p, tile_off, (int*)(smem + SCAN_SCRATCH_OFF));
   const int B = p.batch;
   const int TT = uniform(tile_off[B]);
   const int G = p.grid;
@@ -626,17 +691,27 @@ void mla_decode_kernel(Params p) {
   const int g = (G % 8 == 0) ? ((i & 7) * (G >> 3) + (i >> 3)) : i;
   int x = g * C;
   const int end = min(TT, x + C);
-  bool first = true;
-  while (x < end) {
-    int lo = 0, hi = B;
+  int b = 0, rel = 0;
+  if (x < end) {
+    int lo = 0, hi = B;  // tile_off[lo] <= x < tile_off[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (tile_off[mid] <= x) lo = mid; else hi = mid;
     }
-    const int b = uniform(lo);
+    b = lo;
+    rel = x - tile_off[lo];
+  }
+  b = uniform(b);
+  rel = uniform(rel);
+  __syncthreads();  // the LDS plan is dead from here on
+  bool first = true;
+  while (x < end) {
+    // walk the linear (unit, tile) space forward from request b
     const int L = uniform(p.seq_lens[b]);
+    int r0;
+    const int qb = uniform(request_rows(p, b, r0));
     const int T = ceil_div(L, TILE);
-    const int rel = x - uniform(tile_off[b]);
+    const int units = ceil_div(qb * p.heads, PAIRS_BLOCK);
     const int pb = rel / T;
     const int t0 = rel - pb * T;
     const int t1 = min(T, t0 + (end - x));
@@ -646,6 +721,11 @@ void mla_decode_kernel(Params p) {
     while (!process_segment<FP8, PS>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
     }
     x += t1 - t0;
+    rel += t1 - t0;
+    if (rel >= units * T) {
+      ++b;
+      rel = 0;
+    }
     first = false;
   }
 }
