@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads (lines on stderr)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed steps, run 3 plain device-to-device copies of this many bytes "
+                         "(HBM-counter calibration under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
@@ -183,6 +186,15 @@ def main():
                 continue
             r = run_workload(name, args.steps, args.warmup, False)
             log("[bench-extra] " + json.dumps(r))
+    if args.copy_bytes > 0:
+        n = (args.copy_bytes + 15) // 16 * 16
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copies: 3 x {n} bytes")
     print(json.dumps(res), flush=True)
 
 

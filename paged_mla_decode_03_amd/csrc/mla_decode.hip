@@ -9,23 +9,28 @@
 // same rows.  All H heads share one latent KV head, so one KV tile in LDS feeds
 // every pair of the request.
 //
-// Kernel design (one workgroup per compute unit, persistent):
+// Kernel design (one 4-wave workgroup per compute unit, persistent):
 //   * Work plan, on device: every workgroup scans seq_lens / qo_indptr into LDS
-//     (tiles of 64 KV rows per "unit" = request x block of 128 pairs), then owns
-//     an equal, contiguous range of the linearised (unit, tile) space.  A unit cut
-//     by range boundaries is written as partials and merged by a second kernel.
-//     No device-to-host read anywhere.
-//   * Loader: each wave streams its 16 rows of the next tile straight into LDS
-//     with global_load_lds_dwordx4 (16 B per lane, one page per wave per tile, so
-//     the page base is a scalar); double-buffered; rows past seq_len are never
+//     (tiles of 32 KV rows per "unit" = request x block of 128 (row, head)
+//     pairs), then owns an equal, contiguous range of the linearised
+//     (unit, tile) space.  A unit cut by range boundaries is written as partials
+//     and merged by a second kernel.  No device-to-host read anywhere.
+//   * Each wave owns 32 pairs with all 576 query dims in VGPRs (MFMA B operand)
+//     and all 512 output dims in accumulators, so a KV tile is read from HBM
+//     once per unit and no logits are exchanged between waves.
+//   * Loader: each wave streams 8 rows of a tile straight into LDS with
+//     global_load_lds_dwordx4 (16 B per lane; the page base is wave-uniform);
+//     a 4-buffer ring keeps two tiles in flight; rows past seq_len are never
 //     loaded and are zero-filled instead, so NaN in unused slots cannot leak.
 //     16-byte chunks are XOR-swizzled by row to keep LDS reads conflict-free.
 //   * QK^T: S^T[32 tokens x 32 pairs] per wave on v_mfma_f32_32x32x16_bf16 with
 //     the KV tile as the A operand (rows permuted so the result lands directly in
-//     the B-operand layout P.V needs) and the wave's 32 query pairs held in VGPRs.
-//   * Softmax: exp2 domain (log2 e folded into bmm1), one pair per lane; the
-//     lane halves and the two waves of a pair group exchange maxima and sums; the
-//     running max is only moved (and O rescaled) when it grows by more than 2^8.
+//     the B-operand layout P.V needs); the next tile's QK^T is issued before the
+//     current tile's softmax so the matrix cores run under the VALU work.
+//   * Softmax: exp2 domain (log2 e folded into bmm1), one pair per lane column;
+//     logits are taken relative to a per-pair reference max fixed by the first
+//     visible tile; a logit beyond it by more than 2^32 restarts the segment with
+//     the observed max (never happens for sane inputs; keeps O free of rescales).
 //   * P.V: O^T[512 x 32 pairs] += V^T . P^T on the same MFMA; V^T fragments come
 //     from LDS through ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (fp8).
 //   * fp8 E4M3FN KV is converted exactly to bf16 in registers (v_cvt_pk_f32_fp8),
@@ -44,21 +49,24 @@ namespace {
 constexpr int D_QK = 576;
 constexpr int D_V = 512;
 constexpr int TILE = 32;          // KV rows per LDS tile
-constexpr int NBUF = 4;           // tile buffers: tiles t..t+2 resident or landing, t+3 being issued
-constexpr int THREADS = 256;      // 4 waves
-constexpr int PAIRS_WAVE = 32;   // (row, head) pairs per wave (MFMA N dimension)
-constexpr int PAIRS_BLOCK = 64;  // pairs per unit: 2 pair groups x 32
-constexpr int QK_STEPS = 18;     // 16-dim MFMA steps per wave: half of 576
+constexpr int NBUF = 4;           // ring: tile t+1 resident, t+2/t+3 landing, t in use by P.V
+constexpr int THREADS = 256;      // 4 waves, one per SIMD
+constexpr int WAVES = THREADS / 64;
+constexpr int PAIRS_WAVE = 32;    // (row, head) pairs per wave (MFMA N dimension)
+constexpr int PAIRS_BLOCK = WAVES * PAIRS_WAVE;  // 128 pairs per unit
+constexpr int QK_STEPS = 36;      // 16-dim MFMA steps over 576 dims (32 latent + 4 RoPE)
+constexpr int PV_BLOCKS = 16;     // 32-dim output blocks over 512 dims
 constexpr int ROWB_BF16 = D_QK * 2;            // 1152
 constexpr int ROWB_FP8 = D_QK;                 // 576
 constexpr int TILEB = TILE * ROWB_BF16;        // 36864 bytes per buffer (fp8 tiles use half)
+constexpr int MERGE_THREADS = 256;     // merge kernel: one wave per (row, head)
 constexpr int PLAN_INTS = MLA_MAX_BATCH + 1;
-constexpr int XS_OFF = NBUF * TILEB;           // partial-logit exchange: [4 waves][4][64 lanes][16 B]
-constexpr int LDS_BYTES = XS_OFF + 4 * 4096;   // 163840: the whole LDS of a CU
-// The work-plan scan (prologue only) and the end-of-segment flags alias the
-// tile buffers / the exchange area when those are idle.
+constexpr int FLAGS_OFF = NBUF * TILEB;        // end-of-segment flags
+constexpr int LDS_BYTES = FLAGS_OFF + 64;
+// The work-plan scan (prologue only) aliases the tile buffers while they are idle.
 constexpr int PLAN_SCRATCH_OFF = 0;
-constexpr int SCAN_SCRATCH_OFF = PLAN_INTS * 4 + 60;
+constexpr int UNIT_SCRATCH_OFF = PLAN_INTS * 4 + 60;
+constexpr int SCAN_SCRATCH_OFF = UNIT_SCRATCH_OFF + PLAN_INTS * 4 + 60;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 // A segment is redone with a raised reference max only when a logit beats the
@@ -66,6 +74,7 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_THRESHOLD = 32.0f;
 
 static_assert(LDS_BYTES <= 163840, "LDS budget");
+static_assert(SCAN_SCRATCH_OFF + 2 * THREADS * 4 <= TILEB, "plan scratch fits in one tile buffer");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -83,9 +92,11 @@ struct Params {
   const int32_t* qo_indptr;
   uint16_t* out;
   float* lse;
-  float* ws_o;      // [2G][128][512] fp32 partial O (unnormalised)
-  float* ws_ml;     // [2G][128][2]   partial (max in log2 units, sum)
-  int32_t* ws_plan; // [0] = tiles per workgroup C, [1] = total tiles, [2 + b] = tile offset of request b
+  float* ws_o;      // [G + U][128][512] fp32 O per segment (unnormalised)
+  float* ws_ml;     // [G + U][128][2]   per segment (max in log2 units, sum)
+  int32_t* ws_plan; // [0] = tiles per workgroup C, [1] = total tiles,
+                    // [2 + b] = tile offset of request b (b <= B),
+                    // [3 + B + b] = first global unit of request b (b <= B)
   int32_t batch;
   int32_t heads;
   int32_t q_len_fixed;
@@ -118,17 +129,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(lds_wave_base)
-               : "memory");
-}
-
-// Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
-// Both bases are wave-uniform; readfirstlane pins them to SGPRs even where the
-// call sits under a lane-divergent branch.
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane, with
+// a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.  Both bases
+// are wave-uniform; readfirstlane pins them to SGPRs even where the call sits
+// under a lane-divergent branch.
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_wave_base) {
   const uint64_t sb = (uint64_t)(uintptr_t)sbase;
   const uint64_t sbu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb) |
@@ -138,13 +142,6 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
                :
                : "v"(voff), "s"((const void*)(uintptr_t)sbu), "s"(m0)
                : "memory");
-}
-
-// Wave-uniform int32 load through the scalar cache (block-table entries).
-__device__ __forceinline__ int load_uniform_i32(const int32_t* ptr) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  return v;
 }
 
 template <int N>
@@ -203,6 +200,32 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// ---------------------------------------------------------------- matrix-core ops
+//
+// The MFMAs are issued through inline asm so that the register class of each
+// accumulator is ours to choose: the 512 output accumulators of a wave live in
+// AGPRs, the QK^T accumulator and everything else in VGPRs (with compiler MFMA
+// builtins every accumulator of a kernel allowed more than 256 VGPRs lands in
+// AGPRs, which does not fit here).  The asm carries the gfx950 wait states the
+// compiler would otherwise insert: each MFMA is preceded by s_nop 1 (a VALU
+// write of an A/B operand needs two wait states before the MFMA reads it; the
+// nop issues while the previous MFMA still occupies the matrix core), and
+// mfma_fence() gives the 12 wait states an MFMA result needs before any other
+// instruction reads it.  Back-to-back MFMAs that accumulate into the same
+// registers need none.
+__device__ __forceinline__ void mfma_acc_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_vgpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ f32x16 mfma_first_vgpr(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_fence(f32x16& v) { asm volatile("s_nop 7\n\ts_nop 3" : "+v"(v)); }
+
 // ---------------------------------------------------------------- tile layout
 //
 // One LDS tile buffer holds 32 cache rows split in two blocks:
@@ -210,7 +233,7 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 //   fp8 : latent block [32][512 B]  at 0, RoPE block [32][64 B]  at 16384.
 // A latent row is then one 64-lane x 16 B load (bf16) or half of one (fp8).
 // 16-byte chunks are XOR-swizzled by row so that both operand reads are
-// bank-conflict free (64 banks x 4 B):
+// bank-conflict free:
 //   * the QK^T A read: 16 lanes read the same chunk of 16 different rows;
 //   * the transposed V^T read: one instruction touches 8 rows x 64 B.
 //   bf16 latent: chunk ^ (((row & 3) << 2) | ((row >> 2) & 3))   (4 bits)
@@ -232,40 +255,89 @@ __device__ __forceinline__ void lds_zero16(uint8_t* smem, uint32_t off) {
 
 // ---------------------------------------------------------------- work plan
 
-// tile_off[b] = first linear tile of request b; tile_off[B] = total tiles.
-// A request contributes ceil(q_b*H / 128) units of ceil(L_b / 64) tiles each.
-__device__ void build_plan(const Params& p, int* tile_off, int* scan) {
+// tile_off[b] = first linear tile of request b, tile_off[B] = total tiles;
+// unit_off[b] = first global unit of request b, unit_off[B] = total units.
+// A request contributes ceil(q_b*H / 128) units of ceil(L_b / 32) tiles each.
+__device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* scan) {
   const int tid = threadIdx.x;
   const int B = p.batch;
   const int per = (B + THREADS - 1) / THREADS;
   const int b0 = min(B, tid * per);
   const int b1 = min(B, b0 + per);
-  int local = 0;
+  int tiles = 0, units = 0;
   for (int b = b0; b < b1; ++b) {
     int r0;
     const int qb = request_rows(p, b, r0);
-    local += ceil_div(qb * p.heads, PAIRS_BLOCK) * ceil_div(p.seq_lens[b], TILE);
+    const int u = ceil_div(qb * p.heads, PAIRS_BLOCK);
+    units += u;
+    tiles += u * ceil_div(p.seq_lens[b], TILE);
   }
-  scan[tid] = local;
+  int* scan_t = scan;
+  int* scan_u = scan + THREADS;
+  scan_t[tid] = tiles;
+  scan_u[tid] = units;
   __syncthreads();
   for (int off = 1; off < THREADS; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
+    const int vt = tid >= off ? scan_t[tid - off] : 0;
+    const int vu = tid >= off ? scan_u[tid - off] : 0;
     __syncthreads();
-    scan[tid] += v;
+    scan_t[tid] += vt;
+    scan_u[tid] += vu;
     __syncthreads();
   }
-  int run = scan[tid] - local;
+  int run_t = scan_t[tid] - tiles;
+  int run_u = scan_u[tid] - units;
   for (int b = b0; b < b1; ++b) {
     int r0;
     const int qb = request_rows(p, b, r0);
-    tile_off[b] = run;
-    run += ceil_div(qb * p.heads, PAIRS_BLOCK) * ceil_div(p.seq_lens[b], TILE);
+    const int u = ceil_div(qb * p.heads, PAIRS_BLOCK);
+    tile_off[b] = run_t;
+    unit_off[b] = run_u;
+    run_t += u * ceil_div(p.seq_lens[b], TILE);
+    run_u += u;
   }
-  if (tid == THREADS - 1) tile_off[B] = scan[THREADS - 1];
+  if (tid == THREADS - 1) {
+    tile_off[B] = scan_t[THREADS - 1];
+    unit_off[B] = scan_u[THREADS - 1];
+  }
   __syncthreads();
 }
 
+// ---------------------------------------------------------------- page-id window
+//
+// A segment's block-table entries are read once, 128 at a time, into two
+// VGPRs (lane i holds entries base + i and base + 64 + i); each tile's page id
+// is then a v_readlane, so issuing a tile's loads never waits on memory.
+struct PageWin {
+  int base;  // first block-table index held (wave-uniform)
+  int lo;    // entry base + lane
+  int hi;    // entry base + 64 + lane
+};
+
+// Entries past the request's last page are never read (they may be garbage).
+__device__ __forceinline__ void load_page_window(const Params& p, int b, int npages, int base, PageWin& pw) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* row = p.block_tables + (size_t)b * p.bt_stride;
+  pw.base = base;
+  pw.lo = (base + lane < npages) ? row[base + lane] : 0;
+  pw.hi = (base + 64 + lane < npages) ? row[base + 64 + lane] : 0;
+}
+
 // ---------------------------------------------------------------- tile loader
+
+// Page id of cache row `row` (< L) of request b, from the window (refilled when
+// the row's page lies past it: drain the loads in flight so the refill is the
+// only vector load the following waits can see, then read the next 128).
+template <int PS>
+__device__ __forceinline__ int page_id(const Params& p, int b, int L, int row, PageWin& pw) {
+  int pi = uniform(row / PS - pw.base);
+  if (pi >= 128) {
+    wait_vmcnt<0>();
+    load_page_window(p, b, ceil_div(L, PS), row / PS, pw);
+    pi = 0;
+  }
+  return uniform(pi < 64 ? __builtin_amdgcn_readlane(pw.lo, pi) : __builtin_amdgcn_readlane(pw.hi, pi - 64));
+}
 
 // DMA instructions one wave issues for a full tile.
 template <bool FP8>
@@ -277,7 +349,8 @@ constexpr int tile_loads() { return FP8 ? 5 : 9; }
 // never read from memory (nor is their block-table entry): they are zero-filled.
 // A full tile costs each wave exactly tile_loads<FP8>() DMA instructions.
 template <bool FP8, int PS>
-__device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t) {
+__device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t,
+                                           PageWin& pw) {
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int row0 = t * TILE + 8 * w;
@@ -291,7 +364,7 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
       lds_zero16(smem, rope + lane * 16);
       return;
     }
-    const int page = load_uniform_i32(p.block_tables + (size_t)b * p.bt_stride + row0 / PS);
+    const int page = page_id<PS>(p, b, L, row0, pw);
     const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_BF16;
     const int nvalid = L - row0;
     // swizzles use the row's place in the tile (8w + i)
@@ -322,7 +395,7 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
       if (lane < 32) lds_zero16(smem, rope + lane * 16);
       return;
     }
-    const int page = load_uniform_i32(p.block_tables + (size_t)b * p.bt_stride + row0 / PS);
+    const int page = page_id<PS>(p, b, L, row0, pw);
     const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_FP8;
     const int nvalid = L - row0;
     const int hi = lane >> 5;
@@ -345,28 +418,19 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 
 // ---------------------------------------------------------------- one segment
 //
-// A unit is (request, block of 64 (row, head) pairs).  The four waves form two
-// pair groups of 32 pairs (grp = w >> 1) times two halves (hh = w & 1):
-//   * QK^T: wave (grp, hh) contracts its 32 pairs against a tile over half of
-//     the 576 head dims -- latent dims [256hh, 256hh+256) and RoPE dims
-//     [512+32hh, 512+32hh+32) -- in 18 MFMAs; the two halves add their fp32
-//     partial logits through LDS, so both hold the full S^T of the tile;
-//   * both run the same softmax, so both hold P for all 32 tokens;
-//   * P.V: wave (grp, hh) accumulates O^T for output dims [256hh, 256hh+256).
-// Each wave keeps half of Q (72 VGPRs) and half of O (128 accumulators).
+// A unit is (request, block of 128 (row, head) pairs); wave w owns pairs
+// [32w, 32w+32) of it with the full 576-dim query and the full 512-dim output.
 //
 // Software pipeline over tiles (4 LDS buffers), iteration t:
-//   barrier A  -> tile t+1 is in LDS, tile t-1's buffer is free: issue tile t+3;
-//                 read the partner's partial logits of tile t
-//   softmax(t) alongside QK^T(t+1) on the matrix cores
-//   barrier B  -> the partner has read this wave's exchange slot
-//   write the partial logits of tile t+1; P.V(t)
-// Waves whose pair group is empty run the same barrier and DMA sequence only.
+//   wait + barrier -> tile t+1 is in LDS, tile t-1's buffer is free: issue tile t+3
+//   QK^T(t+1) on the matrix cores, softmax(t) on the VALU alongside
+//   P.V(t)
+// Waves with no pairs run the same barrier and DMA sequence only.
 
 // Per-lane state of an active wave.
 struct SegState {
-  f32x16 acc[8];   // O^T accumulators
-  float m_ref;     // reference max, log2 units (identical in both halves)
+  f32x16 acc[PV_BLOCKS];  // O^T accumulators, 32 output dims each
+  float m_ref;     // reference max, log2 units (identical in both lane halves)
   float m_max;     // largest logit seen, log2 units
   float lsum;      // this lane's share of the softmax denominator
   bool over;       // some logit beat m_ref by more than the threshold
@@ -374,11 +438,10 @@ struct SegState {
 
 template <bool FP8, int PS, bool ACTIVE>
 __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int b, int L, int t0, int t1,
-                                             const bf16x8 (&qf)[QK_STEPS], int n_vis, SegState& st) {
+                                             const bf16x8 (&qf)[QK_STEPS], int n_vis, int min_vis,
+                                             SegState& st, PageWin& pw) {
   constexpr int LOADS = tile_loads<FP8>();
   const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
-  const int hh = w & 1;
   const int h = lane >> 5;
   auto buf_of = [&](int t) -> uint32_t { return (uint32_t)((t - t0) % NBUF) * TILEB; };
 
@@ -390,62 +453,79 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   const int prow = (lr & 16) | (lr & 3) | ((lr & 4) << 1) | ((lr & 8) >> 1);
   const int s16 = lane & 15;
   const int g1 = (lane >> 4) & 1;
-  uint32_t qa_lat, qa_rope0, qa_rope1, tr_base;
-  int qs_lat, tr_sl, tr_cc, tr_z;
+  uint32_t qa_lat, qa_rope, tr_base;
+  int qs_lat, qs_rope, tr_sl, tr_cc, tr_z;
   if (!FP8) {
-    const int sl = swz_lat_bf16(prow), sr = swz_rope_bf16(prow);
-    qa_lat = prow * 1024 + 512 * hh + 16 * (h ^ (sl & 1));
+    const int sl = swz_lat_bf16(prow);
+    qa_lat = prow * 1024 + 16 * (h ^ (sl & 1));
     qs_lat = sl >> 1;
-    qa_rope0 = ROPE_OFF_BF16 + prow * 128 + 16 * ((4 * hh + h) ^ sr);
-    qa_rope1 = ROPE_OFF_BF16 + prow * 128 + 16 * ((4 * hh + 2 + h) ^ sr);
+    qa_rope = ROPE_OFF_BF16 + prow * 128;
+    qs_rope = swz_rope_bf16(prow);
     tr_sl = s16 >> 2;
     tr_cc = 2 * g1 + ((s16 & 3) >> 1);
-    tr_base = (8 * h + tr_sl) * 1024 + 512 * hh + 8 * (s16 & 1);
+    tr_base = (8 * h + tr_sl) * 1024 + 8 * (s16 & 1);
     tr_z = 0;
   } else {
-    qa_lat = prow * 512 + 256 * hh + 8 * h;
+    qa_lat = prow * 512 + 8 * h;
     qs_lat = swz_lat_fp8(prow);
-    const int sr = swz_rope_fp8(prow);
-    qa_rope0 = ROPE_OFF_FP8 + prow * 64 + 16 * ((2 * hh) ^ sr) + 8 * h;
-    qa_rope1 = ROPE_OFF_FP8 + prow * 64 + 16 * ((2 * hh + 1) ^ sr) + 8 * h;
+    qa_rope = ROPE_OFF_FP8 + prow * 64 + 8 * h;
+    qs_rope = swz_rope_fp8(prow);
     tr_z = s16 >> 1;
-    tr_base = (8 * h + tr_z) * 512 + 256 * hh + 8 * (s16 & 1);
+    tr_base = (8 * h + tr_z) * 512 + 8 * (s16 & 1);
     tr_sl = tr_cc = 0;
   }
-  const uint32_t xs_own = XS_OFF + w * 4096 + lane * 16;
-  const uint32_t xs_other = XS_OFF + (w ^ 1) * 4096 + lane * 16;
 
-  // A fragment for 16-dim step kk of this wave (0..15 latent, 16..17 RoPE)
+  // Per-buffer bases: every per-step offset below is the base XORed with a
+  // step constant (the lane-dependent swizzle bits sit in bits that the buffer
+  // offset and the tile rows never touch) plus an instruction immediate, so a
+  // wave keeps a few base registers instead of one address per step.
+  //   bf16 A : base | 32 qs (bits 5..7), step kk: ^ 32(kk&7), + 256(kk>>3)
+  //   bf16 V : base | 64 tr_sl | 16 (tr_cc ^ 2h) (bits 4..7), block d, chunk c:
+  //            ^ 64(d&3), + 256(d>>2) + 16384c; the second half-read ^ 16, + 4096
+  //   fp8  A : base | 16 qs (bits 4..7), step kk: ^ 16 kk
+  //   fp8  V : base | 16 (g1 ^ (8h + tr_z)) (bits 4..7), block d: ^ 32 d, + 8192c
+  const uint32_t a_lane = FP8 ? qa_lat + 16 * qs_lat : qa_lat + 32 * qs_lat;
+  const uint32_t v_lane = FP8 ? tr_base + 16 * (g1 ^ (8 * h + tr_z))
+                              : tr_base + 64 * tr_sl + 16 * (tr_cc ^ (2 * h));
+  // (the empty asm keeps the compiler from folding a known buffer offset into
+  // per-step lane constants that would then stay live across the whole kernel)
+  auto opaque = [](uint32_t v) -> uint32_t {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  // A fragment for 16-dim step kk (0..31 latent, 32..35 RoPE)
   auto load_a = [&](uint32_t buf, int kk) -> u32x4 {
     if (FP8) {
-      const uint32_t off = (kk < 16) ? buf + qa_lat + 16 * (kk ^ qs_lat) : buf + (kk == 16 ? qa_rope0 : qa_rope1);
+      const uint32_t off = (kk < 32) ? ((buf + a_lane) ^ (16u * (kk & 15))) + 256 * (kk >> 4)
+                                     : buf + qa_rope + 16 * ((kk - 32) ^ qs_rope);
       const u32x2 raw = lds_read_b64(smem, off);
       return u32x4{raw[0], raw[1], 0u, 0u};
     } else {
-      const uint32_t off = (kk < 16) ? buf + qa_lat + 256 * (kk >> 3) + 32 * ((kk & 7) ^ qs_lat)
-                                     : buf + (kk == 16 ? qa_rope0 : qa_rope1);
+      const uint32_t off = (kk < 32) ? ((buf + a_lane) ^ (32u * (kk & 7))) + 256 * (kk >> 3)
+                                     : buf + qa_rope + 16 * ((2 * (kk - 32) + h) ^ qs_rope);
       return lds_read_b128(smem, off);
     }
   };
-  // V^T fragment for step = c * 8 + d (chunk c of 16 tokens, dim block d of 32)
+  // V^T fragment for step = c * 16 + d (chunk c of 16 tokens, dim block d of 32)
   auto load_v = [&](uint32_t buf, int step) -> u32x4 {
-    const int c = step >> 3, d = step & 7;
+    const int c = step >> 4, d = step & 15;
     if (FP8) {
-      const uint32_t off = buf + 16 * c * 512 + tr_base + 16 * ((2 * d + g1) ^ (8 * h + tr_z));
+      const uint32_t off = ((buf + v_lane) ^ (32u * (d & 7))) + 256 * (d >> 3) + 16 * c * 512;
       const i32x2 raw = lds_read_tr8(smem, off);
       return u32x4{(uint32_t)raw[0], (uint32_t)raw[1], 0u, 0u};
     } else {
-      const uint32_t off = buf + 16 * c * 1024 + tr_base + 64 * (d & 4) + 64 * ((d & 3) ^ tr_sl);
-      const s16x4 lo = lds_read_tr16(smem, off + 16 * (tr_cc ^ (2 * h)));
-      const s16x4 hi = lds_read_tr16(smem, off + 4 * 1024 + 16 * (tr_cc ^ (2 * h + 1)));
+      const uint32_t base = ((buf + v_lane) ^ (64u * (d & 3))) + 16 * c * 1024 + 256 * (d >> 2);
+      const s16x4 lo = lds_read_tr16(smem, base);
+      const s16x4 hi = lds_read_tr16(smem, (base ^ 16u) + 4 * 1024);
       return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
   auto to_bf16 = [&](const u32x4& raw) -> bf16x8 {
     return FP8 ? fp8x8_to_bf16x8(raw[0], raw[1]) : __builtin_bit_cast(bf16x8, raw);
   };
-  auto qk_partial = [&](uint32_t buf) -> f32x16 {
-    f32x16 s = f32x16{};
+  auto qk = [&](uint32_t buf_in) -> f32x16 {
+    const uint32_t buf = opaque(buf_in);
+    f32x16 s;
     constexpr int GA = 4;  // A fragments read this many steps ahead
     u32x4 araw[GA];
 #pragma unroll
@@ -454,15 +534,11 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     for (int k = 0; k < QK_STEPS; ++k) {
       const u32x4 cur = araw[k % GA];
       if (k + GA < QK_STEPS) araw[k % GA] = load_a(buf, k + GA);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(to_bf16(cur), qf[k], s, 0, 0, 0);
+      if (k == 0) s = mfma_first_vgpr(to_bf16(cur), qf[k]);
+      else mfma_acc_vgpr(s, to_bf16(cur), qf[k]);
     }
+    mfma_fence(s);
     return s;
-  };
-  auto store_partial = [&](const f32x16& v) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *(__attribute__((address_space(3))) f32x4*)((__attribute__((address_space(3))) uint8_t*)smem + xs_own +
-                                                  j * 1024) = f32x4{v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
   };
 
   // Tile t has landed once at most the DMA ops of the n tiles issued after it
@@ -474,83 +550,76 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     else wait_vmcnt<2 * LOADS>();
   };
 
-  // ---- prologue: partial logits of tile t0
-  wait_tile(t0, 2);
-  wait_lgkm0();
-  block_barrier();
-  f32x16 sp = f32x16{};
-  if (ACTIVE) {
-    sp = qk_partial(buf_of(t0));
-    store_partial(sp);
-  }
+  const float c = p.scale_log2;
+  const bool c_pos = c > 0.f;
 
   for (int t = t0; t < t1; ++t) {
-    if (t + 1 < t1) wait_tile(t + 1, 1);
+    wait_tile(t, 2);
     wait_lgkm0();
-    block_barrier();  // A
-    if (t + 3 < t1) issue_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3);
-    if (!ACTIVE) {
-      wait_lgkm0();
-      block_barrier();  // B
-      continue;
-    }
-    // full logits of tile t: own partial + partner's
-    f32x16 s = sp;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 o = *(const __attribute__((address_space(3))) f32x4*)(
-          (const __attribute__((address_space(3))) uint8_t*)smem + xs_other + j * 1024);
-      s[4 * j] += o[0];
-      s[4 * j + 1] += o[1];
-      s[4 * j + 2] += o[2];
-      s[4 * j + 3] += o[3];
-    }
-    // QK^T of the next tile (past the last tile the buffer holds stale rows;
-    // the result is then unused) runs on the matrix cores under the softmax.
-    const f32x16 sn = qk_partial(buf_of(t + 1));
+    block_barrier();  // tile t is in LDS; tile t-1's buffer is free
+    if (t + 3 < t1) issue_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
+    if (!ACTIVE) continue;
+    f32x16 s = qk(buf_of(t));
     // ---------------- softmax (exp2 domain); value k is token 16(k>>3) + 8h + (k&7)
-    const int tok0 = t * TILE + 8 * h;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      float v = s[k] * p.scale_log2;
-      v = (tok0 + 16 * (k >> 3) + (k & 7)) < n_vis ? v : -INFINITY;
-      s[k] = v;
-      mx = fmaxf(mx, v);
-    }
-    mx = fmaxf(mx, other_half(mx));
-    if (st.m_ref == -INFINITY) st.m_ref = mx;  // first visible tile sets the reference
-    st.m_max = fmaxf(st.m_max, mx);
-    st.over = st.over || (mx > st.m_ref + RESCALE_THRESHOLD);
-    const float mbase = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
     bf16x8 pc0, pc1;
+    const int tok0 = t * TILE + 8 * h;
+    if (c_pos && (t + 1) * TILE <= min_vis) {
+      // every token of the tile is visible to every pair of this wave
+      float mx = s[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e0 = __builtin_amdgcn_exp2f(s[j] - mbase);
-      const float e1 = __builtin_amdgcn_exp2f(s[8 + j] - mbase);
-      st.lsum += e0 + e1;
-      pc0[j] = (__bf16)e0;
-      pc1[j] = (__bf16)e1;
+      for (int k = 1; k < 16; ++k) mx = fmaxf(mx, s[k]);
+      mx = fmaxf(mx, other_half(mx)) * c;
+      if (st.m_ref == -INFINITY) st.m_ref = mx;  // first visible tile sets the reference
+      st.m_max = fmaxf(st.m_max, mx);
+      st.over = st.over || (mx > st.m_ref + RESCALE_THRESHOLD);
+      const float nm = -st.m_ref;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c, nm));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 + j], c, nm));
+        st.lsum += e0 + e1;
+        pc0[j] = (__bf16)e0;
+        pc1[j] = (__bf16)e1;
+      }
+    } else {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float v = (tok0 + 16 * (k >> 3) + (k & 7)) < n_vis ? s[k] * c : -INFINITY;
+        s[k] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, other_half(mx));
+      if (st.m_ref == -INFINITY) st.m_ref = mx;
+      st.m_max = fmaxf(st.m_max, mx);
+      st.over = st.over || (mx > st.m_ref + RESCALE_THRESHOLD);
+      const float mbase = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e0 = __builtin_amdgcn_exp2f(s[j] - mbase);
+        const float e1 = __builtin_amdgcn_exp2f(s[8 + j] - mbase);
+        st.lsum += e0 + e1;
+        pc0[j] = (__bf16)e0;
+        pc1[j] = (__bf16)e1;
+      }
     }
-    wait_lgkm0();
-    block_barrier();  // B
-    store_partial(sn);
-    // ---------------- O^T (this wave's 256 dims) += V^T . P^T over the two 16-token chunks
+    // ---------------- O^T += V^T . P^T over the two 16-token chunks
     {
-      const uint32_t buf = buf_of(t);
+      const uint32_t buf = opaque(buf_of(t));
       constexpr int GV = 4;  // V^T fragments read this many steps ahead
       u32x4 vraw[GV];
 #pragma unroll
       for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
 #pragma unroll
-      for (int step = 0; step < 16; ++step) {
+      for (int step = 0; step < 2 * PV_BLOCKS; ++step) {
         const u32x4 cur = vraw[step % GV];
-        if (step + GV < 16) vraw[step % GV] = load_v(buf, step + GV);
-        st.acc[step & 7] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(to_bf16(cur), (step >> 3) ? pc1 : pc0, st.acc[step & 7], 0, 0, 0);
+        if (step + GV < 2 * PV_BLOCKS) vraw[step % GV] = load_v(buf, step + GV);
+        mfma_acc_agpr(st.acc[step & 15], to_bf16(cur), (step >> 4) ? pc1 : pc0);
       }
+      // results land before anything but the next tile's MFMAs can touch them
+      // (the compiler may copy the accumulators once the loop exits)
+      asm volatile("s_nop 7\n\ts_nop 3" ::: "memory");
     }
-    sp = sn;
   }
 }
 
@@ -563,35 +632,40 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
                                                 int slot, float& m_seed) {
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
-  const int grp = w >> 1;
-  const int hh = w & 1;
   const int h = lane >> 5;
   const int col = lane & 31;
   int r0;
   const int qb = request_rows(p, b, r0);
   const int H = p.heads;
   const int npairs = qb * H;
-  const int pair = pb * PAIRS_BLOCK + grp * PAIRS_WAVE + col;
+  const int pair0 = pb * PAIRS_BLOCK + w * PAIRS_WAVE;  // first pair of this wave
+  const int pair = pair0 + col;
   const bool valid = pair < npairs;
+  const bool active = pair0 < npairs;  // wave-uniform
   const int qi = valid ? pair / H : 0;
   const int head = valid ? pair - qi * H : 0;
-  const int n_vis = !valid ? 0 : (p.causal ? L - qb + qi + 1 : L);
-  const bool active = (pb * PAIRS_BLOCK + grp * PAIRS_WAVE) < npairs;  // uniform, same for both halves
+  // visible rows: causal rows see L - q_b + qi + 1; inactive lanes see L (their
+  // zero query gives finite logits and their results are discarded)
+  const int n_vis = !valid ? L : (p.causal ? L - qb + qi + 1 : L);
+  const int min_vis = uniform(p.causal ? L - qb + (active ? pair0 / H : 0) + 1 : L);
 
-  // first three tiles in flight before the query loads
-  issue_tile<FP8, PS>(p, smem, 0, b, L, t0);
-  if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1);
-  if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2);
+  // page ids of the segment, then the first three tiles in flight before the
+  // query loads
+  PageWin pw;
+  load_page_window(p, b, ceil_div(L, PS), uniform((t0 * TILE) / PS), pw);
+  wait_vmcnt<0>();
+  issue_tile<FP8, PS>(p, smem, 0, b, L, t0, pw);
+  if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1, pw);
+  if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2, pw);
 
-  // Query fragments (B operand): lane holds pair `col`; step kk < 16 covers latent
-  // dims 256hh + 16kk + 8h .. +8, steps 16, 17 RoPE dims 512 + 32hh + 16(kk-16) + 8h.
+  // Query fragments (B operand): lane holds pair `col`; step kk < 32 covers latent
+  // dims 16kk + 8h .. +8, steps 32..35 RoPE dims 512 + 16(kk-32) + 8h.
   bf16x8 qf[QK_STEPS];
   {
     const uint16_t* qrow = p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 8 * h;
 #pragma unroll
     for (int k = 0; k < QK_STEPS; ++k) {
-      const int dim = k < 16 ? 256 * hh + 16 * k : 512 + 32 * hh + 16 * (k - 16);
-      const u32x4 v = (valid && active) ? *(const u32x4*)(qrow + dim) : u32x4{0, 0, 0, 0};
+      const u32x4 v = (valid && active) ? *(const u32x4*)(qrow + 16 * k) : u32x4{0, 0, 0, 0};
       qf[k] = __builtin_bit_cast(bf16x8, v);
     }
     // Consume the loads here so no wait on them is left inside the tile loop
@@ -602,16 +676,16 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
 
   SegState st;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.acc[i] = f32x16{};
+  for (int i = 0; i < PV_BLOCKS; ++i) st.acc[i] = f32x16{};
   st.m_ref = m_seed;
   st.m_max = m_seed;
   st.lsum = 0.f;
   st.over = false;
-  if (active) segment_loop<FP8, PS, true>(p, smem, b, L, t0, t1, qf, n_vis, st);
-  else segment_loop<FP8, PS, false>(p, smem, b, L, t0, t1, qf, n_vis, st);
+  if (active) segment_loop<FP8, PS, true>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
+  else segment_loop<FP8, PS, false>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
 
   // ---- segment end: all waves idle on LDS; one flag per wave says "redo"
-  int* flags = (int*)(smem + XS_OFF);
+  int* flags = (int*)(smem + FLAGS_OFF);
   wait_lgkm0();
   block_barrier();
   if (lane == 0) flags[w] = __builtin_amdgcn_ballot_w64(st.over) != 0 ? 1 : 0;
@@ -622,45 +696,26 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
     return false;
   }
 
-  // ---------------- epilogue: the two lane halves hold the two token halves
-  float lsum = st.lsum + other_half(st.lsum);
+  // ---------------- epilogue: the two lane halves hold the two token halves.
+  // O goes out unnormalised, straight from the accumulators; the merge kernel
+  // normalises and rounds every output row.
+  const float lsum = st.lsum + other_half(st.lsum);
   if (!active || !valid) return true;
-  if (slot < 0) {
-    const float inv = p.bmm2 / lsum;
-    uint16_t* op = p.out + ((size_t)(r0 + qi) * H + head) * D_V + 256 * hh;
+  const int pl = w * PAIRS_WAVE + col;
+  float* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
+  for (int d = 0; d < PV_BLOCKS; ++d) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dim = 32 * d + 8 * q4 + 4 * h;
-        u32x2 packed;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const __bf16 lo = (__bf16)(st.acc[d][4 * q4 + 2 * e] * inv);
-          const __bf16 hi = (__bf16)(st.acc[d][4 * q4 + 2 * e + 1] * inv);
-          packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-        *(u32x2*)(op + dim) = packed;
-      }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int dim = 32 * d + 8 * q4 + 4 * h;
+      *(float4*)(wo + dim) =
+          make_float4(st.acc[d][4 * q4], st.acc[d][4 * q4 + 1], st.acc[d][4 * q4 + 2], st.acc[d][4 * q4 + 3]);
     }
-    if (p.lse != nullptr && h == 0 && hh == 0) p.lse[(size_t)(r0 + qi) * H + head] = (st.m_ref + __log2f(lsum)) * LN2;
-  } else {
-    const int pl = grp * PAIRS_WAVE + col;
-    float* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V + 256 * hh;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dim = 32 * d + 8 * q4 + 4 * h;
-        *(float4*)(wo + dim) =
-            make_float4(st.acc[d][4 * q4], st.acc[d][4 * q4 + 1], st.acc[d][4 * q4 + 2], st.acc[d][4 * q4 + 3]);
-      }
-    }
-    if (h == 0 && hh == 0) {
-      float* ml = p.ws_ml + ((size_t)slot * PAIRS_BLOCK + pl) * 2;
-      ml[0] = st.m_ref;
-      ml[1] = lsum;
-    }
+  }
+  if (h == 0) {
+    float* ml = p.ws_ml + ((size_t)slot * PAIRS_BLOCK + pl) * 2;
+    ml[0] = st.m_ref;
+    ml[1] = lsum;
   }
   return true;
 }
@@ -673,13 +728,17 @@ void mla_decode_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   // The plan lives in LDS only until this workgroup has found its starting point.
   int* tile_off = (int*)(smem + PLAN_SCRATCH_OFF);
-  build_plan(p, tile_off, (int*)(smem + SCAN_SCRATCH_OFF));
+  int* unit_off = (int*)(smem + UNIT_SCRATCH_OFF);
+  build_plan(p, tile_off, unit_off, (int*)(smem + SCAN_SCRATCH_OFF));
   const int B = p.batch;
   const int TT = uniform(tile_off[B]);
   const int G = p.grid;
   const int C = max(1, ceil_div(TT, G));
   if (blockIdx.x == 0) {
-    for (int b = threadIdx.x; b <= B; b += THREADS) p.ws_plan[2 + b] = tile_off[b];
+    for (int b = threadIdx.x; b <= B; b += THREADS) {
+      p.ws_plan[2 + b] = tile_off[b];
+      p.ws_plan[3 + B + b] = unit_off[b];
+    }
     if (threadIdx.x == 0) {
       p.ws_plan[0] = C;
       p.ws_plan[1] = TT;
@@ -703,8 +762,8 @@ void mla_decode_kernel(Params p) {
   }
   b = uniform(b);
   rel = uniform(rel);
+  int u_base = uniform(unit_off[b]);  // global unit index of request b's first unit
   __syncthreads();  // the LDS plan is dead from here on
-  bool first = true;
   while (x < end) {
     // walk the linear (unit, tile) space forward from request b
     const int L = uniform(p.seq_lens[b]);
@@ -715,8 +774,9 @@ void mla_decode_kernel(Params p) {
     const int pb = rel / T;
     const int t0 = rel - pb * T;
     const int t1 = min(T, t0 + (end - x));
-    const bool whole = (t0 == 0 && t1 == T);
-    const int slot = whole ? -1 : (first ? 2 * g : 2 * g + 1);
+    // segment (workgroup g, global unit u) has slot g + u: unique, since every
+    // later segment has a larger g or a larger u
+    const int slot = g + u_base + pb;
     float m_seed = -INFINITY;
     while (!process_segment<FP8, PS>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
     }
@@ -725,19 +785,20 @@ void mla_decode_kernel(Params p) {
     if (rel >= units * T) {
       ++b;
       rel = 0;
+      u_base += units;
     }
-    first = false;
   }
 }
 
 // ---------------------------------------------------------------- split merge
 
-// One wave per (query row, head).  Units written whole by the decode kernel are
-// skipped; for split ones: M = max_s m_s, w_s = 2^(m_s - M),
-// out = bmm2 * sum w_s O_s / sum w_s l_s, lse = ln2 * (M + log2 sum w_s l_s).
-__global__ __launch_bounds__(THREADS) void mla_merge_kernel(Params p) {
+// One wave per (query row, head): combine the segments of its unit,
+// M = max_s m_s, w_s = 2^(m_s - M), out = bmm2 * sum w_s O_s / sum w_s l_s,
+// lse = ln2 * (M + log2 sum w_s l_s).  A unit done by one workgroup has a single
+// segment (w = 1): the same formula normalises it.
+__global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6);
+  const int item = blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6);
   const int H = p.heads;
   if (item >= p.total_q * H) return;
   const int row = item / H;
@@ -761,23 +822,20 @@ __global__ __launch_bounds__(THREADS) void mla_merge_kernel(Params p) {
   const int C = p.ws_plan[0];
   const int T = ceil_div(p.seq_lens[b], TILE);
   const int U0 = p.ws_plan[2 + b] + pb * T;
+  const int u = p.ws_plan[3 + p.batch + b] + pb;
   const int g0 = U0 / C;
   const int g1 = (U0 + T - 1) / C;
-  if (g0 == g1) return;
   float M = -INFINITY;
-  for (int g = g0; g <= g1; ++g) {
-    const int slot = 2 * g + ((g == g0 && U0 > g0 * C) ? 1 : 0);
-    M = fmaxf(M, p.ws_ml[((size_t)slot * PAIRS_BLOCK + pl) * 2]);
-  }
+  for (int g = g0; g <= g1; ++g) M = fmaxf(M, p.ws_ml[((size_t)(g + u) * PAIRS_BLOCK + pl) * 2]);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float den = 0.f;
   for (int g = g0; g <= g1; ++g) {
-    const int slot = 2 * g + ((g == g0 && U0 > g0 * C) ? 1 : 0);
-    const float* ml = p.ws_ml + ((size_t)slot * PAIRS_BLOCK + pl) * 2;
+    const size_t slot = (size_t)(g + u);
+    const float* ml = p.ws_ml + (slot * PAIRS_BLOCK + pl) * 2;
     const float m = ml[0];
     const float wgt = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
     den += wgt * ml[1];
-    const float4* o = (const float4*)(p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V + 8 * lane);
+    const float4* o = (const float4*)(p.ws_o + (slot * PAIRS_BLOCK + pl) * D_V + 8 * lane);
     const float4 a = o[0], c = o[1];
     acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
     acc[4] += wgt * c.x; acc[5] += wgt * c.y; acc[6] += wgt * c.z; acc[7] += wgt * c.w;
@@ -830,13 +888,19 @@ struct WsLayout {
   size_t plan_off, ml_off, o_off, total;
 };
 
-WsLayout workspace_layout(int grid) {
+// Upper bound on the units of a launch: every request has at most max_q_len rows.
+int64_t max_units(const mla_decode_dims_t* d, int32_t max_q_len) {
+  return (int64_t)d->batch * (((int64_t)max_q_len * d->num_heads + PAIRS_BLOCK - 1) / PAIRS_BLOCK);
+}
+
+WsLayout workspace_layout(int grid, int64_t units) {
   WsLayout l;
   auto align = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t slots = (size_t)grid + (size_t)units;
   l.plan_off = 0;
-  l.ml_off = align((size_t)(2 + PLAN_INTS) * 4);
-  l.o_off = align(l.ml_off + (size_t)2 * grid * PAIRS_BLOCK * 2 * 4);
-  l.total = align(l.o_off + (size_t)2 * grid * PAIRS_BLOCK * D_V * 4);
+  l.ml_off = align((size_t)(3 + 2 * PLAN_INTS) * 4);
+  l.o_off = align(l.ml_off + slots * PAIRS_BLOCK * 2 * 4);
+  l.total = align(l.o_off + slots * PAIRS_BLOCK * D_V * 4);
   return l;
 }
 
@@ -853,8 +917,7 @@ int validate(const mla_decode_dims_t* d, int32_t max_seq_len, int32_t max_q_len,
   if (packed && d->total_q > (int64_t)d->batch * max_q_len) return MLA_ERR_BAD_Q_LEN;
   if ((int64_t)d->block_table_stride * d->page_size < max_seq_len) return MLA_ERR_BAD_BLOCK_TABLE;
   // 32-bit tile arithmetic on device
-  const int64_t units = (int64_t)d->batch * ((int64_t)max_q_len * d->num_heads + PAIRS_BLOCK - 1) / PAIRS_BLOCK;
-  if (units * ((max_seq_len + TILE - 1) / TILE) >= (int64_t)1 << 30) return MLA_ERR_BAD_SHAPE;
+  if (max_units(d, max_q_len) * ((max_seq_len + TILE - 1) / TILE) >= (int64_t)1 << 30) return MLA_ERR_BAD_SHAPE;
   return MLA_OK;
 }
 
@@ -893,7 +956,7 @@ size_t mla_decode_paged_workspace_size(const mla_decode_dims_t* dims, int32_t ma
   if (validate(dims, max_seq_len, max_q_len, true) != MLA_OK) return 0;
   int grid = 0;
   if (device_grid(&grid) != MLA_OK) return 0;
-  return workspace_layout(grid).total;
+  return workspace_layout(grid, max_units(dims, max_q_len)).total;
 }
 
 int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_tables, const int32_t* seq_lens,
@@ -908,7 +971,7 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
   int grid = 0;
   const int gs = device_grid(&grid);
   if (gs != MLA_OK) return gs;
-  const WsLayout wl = workspace_layout(grid);
+  const WsLayout wl = workspace_layout(grid, max_units(dims, max_q_len));
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
   Params p;
@@ -945,7 +1008,7 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
   }
   if (ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev1, s);
   const int items = dims->total_q * dims->num_heads;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3((items + 3) / 4), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL(mla_merge_kernel, dim3((items + 3) / 4), dim3(MERGE_THREADS), 0, s, p);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

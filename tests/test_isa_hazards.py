@@ -1,0 +1,104 @@
+"""CPU test: the gfx950 assembly of the library carries the MFMA wait states.
+
+The decode kernel issues its MFMAs through inline asm (so it can place the
+output accumulators in AGPRs), which hides them from the compiler's hazard
+recognizer.  This test compiles the library source to gfx950 assembly with the
+build's own flags and runs tests/isa_hazards.py over every kernel.  The checker
+itself is pinned by compiler-generated MFMA code (which must come out clean)
+and by planted hazards (which must be found).
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+import isa_hazards as ih
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "paged_mla_decode_03_amd", "csrc", "mla_decode.hip")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+pytestmark = pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not available")
+
+
+def _compile_asm(src_path, out_path, extra=()):
+    from paged_mla_decode_03_amd import build_lib
+    flags = [f for f in build_lib.FLAGS if f not in ("-shared", "-fPIC")]
+    cmd = [HIPCC] + flags + ["--cuda-device-only", "-S", "-o", out_path, src_path] + list(extra)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    with open(out_path) as f:
+        return f.read()
+
+
+@pytest.fixture(scope="module")
+def library_asm(tmp_path_factory):
+    return _compile_asm(SRC, str(tmp_path_factory.mktemp("asm") / "mla_decode.s"))
+
+
+@pytest.fixture(scope="module")
+def decode_bodies(library_asm):
+    bodies = {n: b for n, b in ih.kernel_bodies(library_asm) if "mla_decode_kernel" in n}
+    assert len(bodies) == 6, sorted(bodies)  # {bf16, fp8} x page size {16, 32, 64}
+    return bodies
+
+
+def test_library_kernels_have_no_mfma_hazards(library_asm, decode_bodies):
+    res = ih.check_asm(library_asm)
+    bad = {k: v for k, v in res.items() if v}
+    assert not bad, {k: v[:3] for k, v in bad.items()}
+    for name, body in decode_bodies.items():
+        assert sum("v_mfma" in l for l in body) >= 68, name  # 36 QK^T + 32 P.V steps per tile
+
+
+PROBE = r'''
+#include <hip/hip_runtime.h>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__global__ __launch_bounds__(64) void probe(f32x16* o, const bf16x8* a, const bf16x8* b, float f) {
+  f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[threadIdx.x], b[threadIdx.x], f32x16{}, 0, 0, 0);
+  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[threadIdx.x + 64], b[threadIdx.x + 64], s, 0, 0, 0);
+  s[0] = s[0] * f;
+  bf16x8 x = a[threadIdx.x + 128];
+  x[0] = (__bf16)f;
+  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b[threadIdx.x], s, 0, 0, 0);
+  o[threadIdx.x] = s;
+}
+'''
+
+
+def test_checker_accepts_compiler_scheduled_mfma(tmp_path):
+    """The compiler inserts its own wait states around builtin MFMAs; the
+    checker's rules must not be stricter than the hardware's."""
+    src = tmp_path / "probe.hip"
+    src.write_text(PROBE)
+    asm = _compile_asm(str(src), str(tmp_path / "probe.s"))
+    res = {k: v for k, v in ih.check_asm(asm, "probe").items()}
+    assert res and all(not v for v in res.values()), res
+
+
+def test_checker_finds_planted_hazards(decode_bodies):
+    body = next(iter(decode_bodies.values()))
+    assert not ih.check_body(body)
+    # a read of an MFMA result right after the MFMA
+    i = next(k for k, l in enumerate(body) if "v_mfma" in l)
+    dst = body[i].split()[1].rstrip(",")
+    m = re.match(r"([va])\[(\d+)", dst)
+    reg = f"{m.group(1)}{m.group(2)}"
+    read = f"\tv_mov_b32_e32 v0, {reg}" if reg[0] == "v" else f"\tv_accvgpr_read_b32 v0, {reg}"
+    assert ih.check_body(body[:i + 1] + [read] + body[i + 1:])
+    # the fences removed: results are read too early somewhere
+    stripped = [l for l in body if not re.match(r"\s*s_nop 7\s*$", l)]
+    assert ih.check_body(stripped)
+    # a VALU write of an A operand right before the MFMA that reads it
+    a_op = body[i].split(",")[1].strip()
+    m = re.match(r"v\[(\d+)", a_op)
+    if m:
+        write = f"\tv_mov_b32_e32 v{m.group(1)}, 0"
+        j = i
+        while re.match(r"\s*s_nop", body[j - 1]):
+            j -= 1
+        assert ih.check_body(body[:j] + [write] + body[i:])
