@@ -32,8 +32,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """Time the oracle as it stands on whole requests of w until ~budget_s."""
+def cpu_baseline(w, budget_s=10.0):
+    """Time the oracle as it stands on whole requests of w (cycling through the
+    batch) until about budget_s seconds of CPU work have been spent."""
     import numpy as np
     import oracle
     try:
@@ -42,18 +43,56 @@ def cpu_baseline(w, budget_s=15.0):
     except Exception:
         threads = os.cpu_count() or 1
     prob = oracle.MlaProblem(**w.oracle_problem_kwargs())
-    done, tokens = [], 0
+    calls, tokens = 0, 0
     t0 = time.perf_counter()
-    for b in range(w.batch):
+    while True:
+        b = calls % w.batch
         oracle.reference_decode(prob, requests=[b])
-        done.append(b)
+        calls += 1
         tokens += int(w.seq_lens[b])
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"requests 0..{done[-1]} of {w.name} ({len(done)} of {w.batch} requests, "
-                      f"{tokens} KV tokens, {dt:.1f} s, float64 NumPy)"}
+            "sample": f"{calls} whole requests of {w.name} (cycling through its {w.batch}), "
+                      f"{tokens} KV tokens in {dt:.1f} s, float64 NumPy"}
+
+
+KERNEL_SRC = os.path.join(ROOT, "paged_mla_decode_03_amd", "csrc", "mla_decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_sha256():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def profiled_traffic(workload):
+    """HBM bytes per decode-kernel launch from a committed rocprofv3 summary, or
+    None when no summary matches both the workload and the current kernel source.
+
+    A summary carries one line
+      bench-traffic: workload=W kernel_sha256=H fetch_kib=F write_kib=X fetch_scale=a write_scale=b
+    where F and X are the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch)
+    and a, b the factors that turn them into bytes for a plain copy of known size.
+    """
+    if not os.path.isdir(PROFILES):
+        return None
+    sha = kernel_source_sha256()
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(PROFILES, name)) as f:
+            for line in f:
+                line = line.strip().strip("`")
+                if not line.startswith("bench-traffic:"):
+                    continue
+                kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
+                if kv.get("workload") == workload and kv.get("kernel_sha256") == sha:
+                    return int((float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                                float(kv["write_kib"]) * float(kv["write_scale"])) * 1024)
+    return None
 
 
 def run_workload(name, steps, warmup, want_cpu):
@@ -122,11 +161,11 @@ def run_workload(name, steps, warmup, want_cpu):
     if t_hbm >= t_mfma:
         achieved = counts["bytes"] / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(name)}
     else:
         achieved = counts["flops"] / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": achieved / PEAK_MFMA_TFLOPS["bf16"], "traffic": None}
+                "frac": achieved / PEAK_MFMA_TFLOPS["bf16"], "traffic": profiled_traffic(name)}
     spec = WORKLOADS[name]
     res = {
         "metric": METRIC,
@@ -150,6 +189,7 @@ def run_workload(name, steps, warmup, want_cpu):
         "tflops": counts["flops"] / (ms_step * 1e-3) / 1e12,
         "gbps": counts["bytes"] / (ms_step * 1e-3) / 1e9,
         "decode_kernel_ms": kern_ms,
+        "kernel_source_sha256": kernel_source_sha256(),
         "roofline": roof,
     }
     if want_cpu:

@@ -92,7 +92,7 @@ struct Params {
   const int32_t* qo_indptr;
   uint16_t* out;
   float* lse;
-  float* ws_o;      // [G + U][128][512] fp32 O per segment (unnormalised)
+  uint16_t* ws_o;   // [G + U][128][512] bf16 O per segment (unnormalised)
   float* ws_ml;     // [G + U][128][2]   per segment (max in log2 units, sum)
   int32_t* ws_plan; // [0] = tiles per workgroup C, [1] = total tiles,
                     // [2 + b] = tile offset of request b (b <= B),
@@ -697,19 +697,29 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   }
 
   // ---------------- epilogue: the two lane halves hold the two token halves.
-  // O goes out unnormalised, straight from the accumulators; the merge kernel
-  // normalises and rounds every output row.
+  // O goes out unnormalised as bf16 (its scale is relative to m_ref, and the
+  // merge kernel divides by the summed denominator), one 32-dim block at a
+  // time: the empty asm keeps each block in AGPRs until its turn, so only 16
+  // accumulators are copied to VGPRs at once.
   const float lsum = st.lsum + other_half(st.lsum);
   if (!active || !valid) return true;
   const int pl = w * PAIRS_WAVE + col;
-  float* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V;
+  uint16_t* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V;
 #pragma unroll
   for (int d = 0; d < PV_BLOCKS; ++d) {
+    asm volatile("" : "+a"(st.acc[d]));
+    const f32x16 v = st.acc[d];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int dim = 32 * d + 8 * q4 + 4 * h;
-      *(float4*)(wo + dim) =
-          make_float4(st.acc[d][4 * q4], st.acc[d][4 * q4 + 1], st.acc[d][4 * q4 + 2], st.acc[d][4 * q4 + 3]);
+      u32x2 packed;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const __bf16 lo = (__bf16)v[4 * q4 + 2 * e];
+        const __bf16 hi = (__bf16)v[4 * q4 + 2 * e + 1];
+        packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      *(u32x2*)(wo + dim) = packed;
     }
   }
   if (h == 0) {
@@ -835,10 +845,12 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
     const float m = ml[0];
     const float wgt = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
     den += wgt * ml[1];
-    const float4* o = (const float4*)(p.ws_o + (slot * PAIRS_BLOCK + pl) * D_V + 8 * lane);
-    const float4 a = o[0], c = o[1];
-    acc[0] += wgt * a.x; acc[1] += wgt * a.y; acc[2] += wgt * a.z; acc[3] += wgt * a.w;
-    acc[4] += wgt * c.x; acc[5] += wgt * c.y; acc[6] += wgt * c.z; acc[7] += wgt * c.w;
+    const u32x4 o = *(const u32x4*)(p.ws_o + (slot * PAIRS_BLOCK + pl) * D_V + 8 * lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += wgt * __uint_as_float(o[e] << 16);
+      acc[2 * e + 1] += wgt * __uint_as_float(o[e] & 0xffff0000u);
+    }
   }
   const float inv = p.bmm2 / den;
   u32x4 packed;
@@ -900,7 +912,7 @@ WsLayout workspace_layout(int grid, int64_t units) {
   l.plan_off = 0;
   l.ml_off = align((size_t)(3 + 2 * PLAN_INTS) * 4);
   l.o_off = align(l.ml_off + slots * PAIRS_BLOCK * 2 * 4);
-  l.total = align(l.o_off + slots * PAIRS_BLOCK * D_V * 4);
+  l.total = align(l.o_off + slots * PAIRS_BLOCK * D_V * 2);
   return l;
 }
 
@@ -985,7 +997,7 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
   uint8_t* ws = (uint8_t*)workspace;
   p.ws_plan = (int32_t*)(ws + wl.plan_off);
   p.ws_ml = (float*)(ws + wl.ml_off);
-  p.ws_o = (float*)(ws + wl.o_off);
+  p.ws_o = (uint16_t*)(ws + wl.o_off);
   p.batch = dims->batch;
   p.heads = dims->num_heads;
   p.q_len_fixed = qo_indptr ? max_q_len : dims->q_len_fixed;
