@@ -61,7 +61,9 @@ constexpr int ROWB_FP8 = D_QK;                 // 576
 constexpr int TILEB = TILE * ROWB_BF16;        // 36864 bytes per buffer (fp8 tiles use half)
 constexpr int MERGE_THREADS = 256;     // merge kernel: one wave per (row, head)
 constexpr int PLAN_INTS = MLA_MAX_BATCH + 1;
-constexpr int FLAGS_OFF = NBUF * TILEB;        // end-of-segment flags
+constexpr int PSLOT_OFF = NBUF * TILEB;        // P exchange: [4 waves][2 KB] bf16 P of a tile
+constexpr int PSLOT_BYTES = 2048;
+constexpr int FLAGS_OFF = PSLOT_OFF + WAVES * PSLOT_BYTES;  // end-of-segment flags
 constexpr int LDS_BYTES = FLAGS_OFF + 64;
 // The work-plan scan (prologue only) aliases the tile buffers while they are idle.
 constexpr int PLAN_SCRATCH_OFF = 0;
@@ -143,6 +145,12 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
                : "v"(voff), "s"((const void*)(uintptr_t)sbu), "s"(m0)
                : "memory");
 }
+
+// vmcnt(0) through the builtin, which the compiler's own wait analysis sees:
+// registers loaded before it are then known complete, so it inserts no wait
+// for them inside the tile loop (where any vmcnt wait would also drain the
+// tiles' DMA, which the compiler does not know about).
+__device__ __forceinline__ void drain_vector_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -321,6 +329,7 @@ __device__ __forceinline__ void load_page_window(const Params& p, int b, int npa
   pw.base = base;
   pw.lo = (base + lane < npages) ? row[base + lane] : 0;
   pw.hi = (base + 64 + lane < npages) ? row[base + 64 + lane] : 0;
+  drain_vector_loads();
 }
 
 // ---------------------------------------------------------------- tile loader
@@ -343,18 +352,28 @@ __device__ __forceinline__ int page_id(const Params& p, int b, int L, int row, P
 template <bool FP8>
 constexpr int tile_loads() { return FP8 ? 5 : 9; }
 
-// Start the loads of tile t of request b into the LDS buffer at byte offset buf.
-// Wave w fills rows [8w, 8w+8), which always sit in one page (page_size is a
-// multiple of 16), so the page base is wave-uniform.  Rows at or past seq_len are
-// never read from memory (nor is their block-table entry): they are zero-filled.
-// A full tile costs each wave exactly tile_loads<FP8>() DMA instructions.
+// A wave's share of one tile load: rows [8w, 8w+8) of tile t, which always sit
+// in one page (page_size is a multiple of 16), so the page base is wave-uniform.
+// prepare_tile() does everything except the DMA of a full 8-row share: rows at
+// or past seq_len are never read from memory (nor is their block-table entry)
+// and are zero-filled; a share cut by seq_len is loaded at once.  A full share
+// is returned for issue_tile_part(), one DMA instruction per call, so that the
+// instructions can be spread between MFMAs: a burst of them stalls the wave's
+// instruction stream while the CU's address unit works through them.
+struct TileLoad {
+  const uint8_t* pg;  // global address of the share's first row; null: nothing left to issue
+  uint32_t lat;       // LDS byte address of the share's first latent row
+  uint32_t rope;      // LDS byte address of the share's RoPE rows
+};
+
 template <bool FP8, int PS>
-__device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t,
-                                           PageWin& pw) {
+__device__ __forceinline__ TileLoad prepare_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t,
+                                                 PageWin& pw) {
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int row0 = t * TILE + 8 * w;
   const uint32_t lds0 = lds_addr(smem);
+  TileLoad tl{nullptr, 0u, 0u};
   if (!FP8) {
     const uint32_t lat = buf + 8 * w * 1024;
     const uint32_t rope = buf + ROPE_OFF_BF16 + 8 * w * 128;
@@ -362,22 +381,15 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 #pragma unroll
       for (int i = 0; i < 8; ++i) lds_zero16(smem, lat + i * 1024 + lane * 16);
       lds_zero16(smem, rope + lane * 16);
-      return;
+      return tl;
     }
     const int page = page_id<PS>(p, b, L, row0, pw);
     const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_BF16;
     const int nvalid = L - row0;
+    if (nvalid >= 8) return TileLoad{pg, lds0 + lat, lds0 + rope};
     // swizzles use the row's place in the tile (8w + i)
     const int rr = lane >> 3;  // RoPE: 8 lanes per row
     const uint32_t rope_off = (uint32_t)(rr * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_rope_bf16(8 * w + rr)) << 4));
-    if (nvalid >= 8) {
-      // all 8 rows live: scalar row base, 32-bit lane offset, no branches
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        dma16_s(pg + i * ROWB_BF16, (uint32_t)((lane ^ swz_lat_bf16(8 * w + i)) << 4), lds0 + lat + i * 1024);
-      dma16_s(pg, rope_off, lds0 + rope);
-      return;
-    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < nvalid)
@@ -393,17 +405,18 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 #pragma unroll
       for (int i = 0; i < 4; ++i) lds_zero16(smem, lat + i * 1024 + lane * 16);
       if (lane < 32) lds_zero16(smem, rope + lane * 16);
-      return;
+      return tl;
     }
     const int page = page_id<PS>(p, b, L, row0, pw);
     const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_FP8;
     const int nvalid = L - row0;
+    if (nvalid >= 8) return TileLoad{pg, lds0 + lat, lds0 + rope};
     const int hi = lane >> 5;
     const int rr = lane >> 2;  // RoPE: 4 lanes per row, 32 lanes
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 2 * i + hi;
-      if (nvalid >= 8 || r < nvalid)
+      if (r < nvalid)
         dma16_s(pg + 2 * i * ROWB_FP8, (uint32_t)(hi * ROWB_FP8 + (((lane & 31) ^ swz_lat_fp8(8 * w + r)) << 4)),
                 lds0 + lat + i * 1024);
       else lds_zero16(smem, lat + i * 1024 + lane * 16);
@@ -414,6 +427,42 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
       else lds_zero16(smem, rope + lane * 16);
     }
   }
+  return tl;
+}
+
+// DMA instruction k (0 .. tile_loads<FP8>() - 1) of a full share.
+template <bool FP8>
+__device__ __forceinline__ void issue_tile_part(const TileLoad& tl, int k) {
+  if (tl.pg == nullptr) return;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  if (!FP8) {
+    if (k < 8) {
+      dma16_s(tl.pg + k * ROWB_BF16, (uint32_t)((lane ^ swz_lat_bf16(8 * w + k)) << 4), tl.lat + k * 1024);
+    } else {
+      const int rr = lane >> 3;
+      dma16_s(tl.pg, (uint32_t)(rr * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_rope_bf16(8 * w + rr)) << 4)), tl.rope);
+    }
+  } else {
+    const int hi = lane >> 5;
+    if (k < 4) {
+      dma16_s(tl.pg + 2 * k * ROWB_FP8,
+              (uint32_t)(hi * ROWB_FP8 + (((lane & 31) ^ swz_lat_fp8(8 * w + 2 * k + hi)) << 4)), tl.lat + k * 1024);
+    } else if (lane < 32) {
+      const int rr = lane >> 2;
+      dma16_s(tl.pg, (uint32_t)(rr * ROWB_FP8 + 512 + (((lane & 3) ^ swz_rope_fp8(8 * w + rr)) << 4)), tl.rope);
+    }
+  }
+}
+
+// A whole tile load at once (prologue, and waves without MFMA work).
+// A full tile costs each wave exactly tile_loads<FP8>() DMA instructions.
+template <bool FP8, int PS>
+__device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t,
+                                           PageWin& pw) {
+  const TileLoad tl = prepare_tile<FP8, PS>(p, smem, buf, b, L, t, pw);
+#pragma unroll
+  for (int k = 0; k < tile_loads<FP8>(); ++k) issue_tile_part<FP8>(tl, k);
 }
 
 // ---------------------------------------------------------------- one segment
@@ -429,7 +478,7 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 
 // Per-lane state of an active wave.
 struct SegState {
-  f32x16 acc[PV_BLOCKS];  // O^T accumulators, 32 output dims each
+  f32x16 acc[PV_BLOCKS];  // O^T accumulators: [2d + j] = dim block d of this wave's half, pair block j
   float m_ref;     // reference max, log2 units (identical in both lane halves)
   float m_max;     // largest logit seen, log2 units
   float lsum;      // this lane's share of the softmax denominator
@@ -442,6 +491,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
                                              SegState& st, PageWin& pw) {
   constexpr int LOADS = tile_loads<FP8>();
   const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
   const int h = lane >> 5;
   auto buf_of = [&](int t) -> uint32_t { return (uint32_t)((t - t0) % NBUF) * TILEB; };
 
@@ -480,13 +530,17 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   // offset and the tile rows never touch) plus an instruction immediate, so a
   // wave keeps a few base registers instead of one address per step.
   //   bf16 A : base | 32 qs (bits 5..7), step kk: ^ 32(kk&7), + 256(kk>>3)
-  //   bf16 V : base | 64 tr_sl | 16 (tr_cc ^ 2h) (bits 4..7), block d, chunk c:
-  //            ^ 64(d&3), + 256(d>>2) + 16384c; the second half-read ^ 16, + 4096
+  //   bf16 V : base | 64 tr_sl | 16 (tr_cc ^ 2h) (bits 4..7) + 512 dh, block d of the
+  //            half, chunk c: ^ 64(d&3), + 256(d>>2) + 16384c; second half-read ^ 16, + 4096
   //   fp8  A : base | 16 qs (bits 4..7), step kk: ^ 16 kk
-  //   fp8  V : base | 16 (g1 ^ (8h + tr_z)) (bits 4..7), block d: ^ 32 d, + 8192c
+  //   fp8  V : base | 16 (g1 ^ (8h + tr_z)) (bits 4..7) + 256 dh, block d: ^ 32 d, + 8192c
   const uint32_t a_lane = FP8 ? qa_lat + 16 * qs_lat : qa_lat + 32 * qs_lat;
-  const uint32_t v_lane = FP8 ? tr_base + 16 * (g1 ^ (8 * h + tr_z))
-                              : tr_base + 64 * tr_sl + 16 * (tr_cc ^ (2 * h));
+  const int sub = w & 1;  // which 32 pairs of the 64-pair group this wave's QK^T covers
+  const uint32_t ps_own = PSLOT_OFF + w * PSLOT_BYTES + lane * 16;
+  const uint32_t ps_other = PSLOT_OFF + (w ^ 1) * PSLOT_BYTES + lane * 16;
+  const int dh = w & 1;  // P.V output half: dims [256 dh, 256 dh + 256)
+  const uint32_t v_lane = FP8 ? tr_base + 16 * (g1 ^ (8 * h + tr_z)) + 256 * dh
+                              : tr_base + 64 * tr_sl + 16 * (tr_cc ^ (2 * h)) + 512 * dh;
   // (the empty asm keeps the compiler from folding a known buffer offset into
   // per-step lane constants that would then stay live across the whole kernel)
   auto opaque = [](uint32_t v) -> uint32_t {
@@ -506,11 +560,12 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       return lds_read_b128(smem, off);
     }
   };
-  // V^T fragment for step = c * 16 + d (chunk c of 16 tokens, dim block d of 32)
+  // V^T fragment for step = c * 8 + d (chunk c of 16 tokens, dim block d of 32 in this
+  // wave's output half)
   auto load_v = [&](uint32_t buf, int step) -> u32x4 {
-    const int c = step >> 4, d = step & 15;
+    const int c = step >> 3, d = step & 7;
     if (FP8) {
-      const uint32_t off = ((buf + v_lane) ^ (32u * (d & 7))) + 256 * (d >> 3) + 16 * c * 512;
+      const uint32_t off = ((buf + v_lane) ^ (32u * d)) + 16 * c * 512;
       const i32x2 raw = lds_read_tr8(smem, off);
       return u32x4{(uint32_t)raw[0], (uint32_t)raw[1], 0u, 0u};
     } else {
@@ -523,7 +578,9 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   auto to_bf16 = [&](const u32x4& raw) -> bf16x8 {
     return FP8 ? fp8x8_to_bf16x8(raw[0], raw[1]) : __builtin_bit_cast(bf16x8, raw);
   };
-  auto qk = [&](uint32_t buf_in) -> f32x16 {
+  // QK^T of the tile in buf; the DMA instructions of the pending tile load go
+  // out one every four MFMAs
+  auto qk = [&](uint32_t buf_in, const TileLoad& tl) -> f32x16 {
     const uint32_t buf = opaque(buf_in);
     f32x16 s;
     constexpr int GA = 4;  // A fragments read this many steps ahead
@@ -536,6 +593,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       if (k + GA < QK_STEPS) araw[k % GA] = load_a(buf, k + GA);
       if (k == 0) s = mfma_first_vgpr(to_bf16(cur), qf[k]);
       else mfma_acc_vgpr(s, to_bf16(cur), qf[k]);
+      if ((k & 3) == 3 && (k >> 2) < LOADS) issue_tile_part<FP8>(tl, k >> 2);
     }
     mfma_fence(s);
     return s;
@@ -557,9 +615,16 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     wait_tile(t, 2);
     wait_lgkm0();
     block_barrier();  // tile t is in LDS; tile t-1's buffer is free
-    if (t + 3 < t1) issue_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
-    if (!ACTIVE) continue;
-    f32x16 s = qk(buf_of(t));
+    TileLoad tl{nullptr, 0u, 0u};
+    if (t + 3 < t1) tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
+    if (!ACTIVE) {
+#pragma unroll
+      for (int k = 0; k < LOADS; ++k) issue_tile_part<FP8>(tl, k);
+      wait_lgkm0();
+      block_barrier();  // P of tile t posted
+      continue;
+    }
+    f32x16 s = qk(buf_of(t), tl);
     // ---------------- softmax (exp2 domain); value k is token 16(k>>3) + 8h + (k&7)
     bf16x8 pc0, pc1;
     const int tok0 = t * TILE + 8 * h;
@@ -603,7 +668,22 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
         pc1[j] = (__bf16)e1;
       }
     }
-    // ---------------- O^T += V^T . P^T over the two 16-token chunks
+    // ---------------- P exchange: the partner wave (w ^ 1) owns the other 32 pairs
+    // of this 64-pair group; each wave posts its P and reads the partner's
+    *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own) = pc0;
+    *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own + 1024) =
+        pc1;
+    wait_lgkm0();
+    block_barrier();  // P of tile t posted
+    const bf16x8 pp0 = *(const __attribute__((address_space(3))) bf16x8*)(
+        (const __attribute__((address_space(3))) uint8_t*)smem + ps_other);
+    const bf16x8 pp1 = *(const __attribute__((address_space(3))) bf16x8*)(
+        (const __attribute__((address_space(3))) uint8_t*)smem + ps_other + 1024);
+    // pair block j of the group: j == sub is this wave's own P
+    const bf16x8 b00 = sub ? pp0 : pc0, b01 = sub ? pp1 : pc1;  // block 0, chunks 0 / 1
+    const bf16x8 b10 = sub ? pc0 : pp0, b11 = sub ? pc1 : pp1;  // block 1
+    // ---------------- O^T (this wave's 256 dims, both pair blocks) += V^T . P^T:
+    // each V^T fragment feeds two MFMAs
     {
       const uint32_t buf = opaque(buf_of(t));
       constexpr int GV = 4;  // V^T fragments read this many steps ahead
@@ -611,10 +691,13 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
 #pragma unroll
       for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
 #pragma unroll
-      for (int step = 0; step < 2 * PV_BLOCKS; ++step) {
+      for (int step = 0; step < PV_BLOCKS; ++step) {
         const u32x4 cur = vraw[step % GV];
-        if (step + GV < 2 * PV_BLOCKS) vraw[step % GV] = load_v(buf, step + GV);
-        mfma_acc_agpr(st.acc[step & 15], to_bf16(cur), (step >> 4) ? pc1 : pc0);
+        if (step + GV < PV_BLOCKS) vraw[step % GV] = load_v(buf, step + GV);
+        const int d = step & 7;
+        const bf16x8 v = to_bf16(cur);
+        mfma_acc_agpr(st.acc[2 * d], v, (step >> 3) ? b01 : b00);
+        mfma_acc_agpr(st.acc[2 * d + 1], v, (step >> 3) ? b11 : b10);
       }
       // results land before anything but the next tile's MFMAs can touch them
       // (the compiler may copy the accumulators once the loop exits)
@@ -638,22 +721,24 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   const int qb = request_rows(p, b, r0);
   const int H = p.heads;
   const int npairs = qb * H;
-  const int pair0 = pb * PAIRS_BLOCK + w * PAIRS_WAVE;  // first pair of this wave
+  const int pair0 = pb * PAIRS_BLOCK + w * PAIRS_WAVE;  // first pair of this wave's QK^T
   const int pair = pair0 + col;
   const bool valid = pair < npairs;
-  const bool active = pair0 < npairs;  // wave-uniform
+  // a 64-pair group (waves 2g, 2g+1) runs when any of its pairs is live: the
+  // wave that holds its QK^T pairs and the partner that shares its P.V
+  const int gpair0 = pb * PAIRS_BLOCK + (w >> 1) * 2 * PAIRS_WAVE;
+  const bool active = gpair0 < npairs;  // wave-uniform, same for both waves of the group
   const int qi = valid ? pair / H : 0;
   const int head = valid ? pair - qi * H : 0;
   // visible rows: causal rows see L - q_b + qi + 1; inactive lanes see L (their
   // zero query gives finite logits and their results are discarded)
   const int n_vis = !valid ? L : (p.causal ? L - qb + qi + 1 : L);
-  const int min_vis = uniform(p.causal ? L - qb + (active ? pair0 / H : 0) + 1 : L);
+  const int min_vis = uniform((p.causal && pair0 < npairs) ? L - qb + pair0 / H + 1 : L);
 
   // page ids of the segment, then the first three tiles in flight before the
   // query loads
   PageWin pw;
   load_page_window(p, b, ceil_div(L, PS), uniform((t0 * TILE) / PS), pw);
-  wait_vmcnt<0>();
   issue_tile<FP8, PS>(p, smem, 0, b, L, t0, pw);
   if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1, pw);
   if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2, pw);
@@ -668,10 +753,12 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
       const u32x4 v = (valid && active) ? *(const u32x4*)(qrow + 16 * k) : u32x4{0, 0, 0, 0};
       qf[k] = __builtin_bit_cast(bf16x8, v);
     }
-    // Consume the loads here so no wait on them is left inside the tile loop
-    // (where it would also wait for the tiles' DMA).
+    // Wait for the loads here and redefine the registers through an empty asm,
+    // so the compiler sees no load pending on them inside the tile loop (a
+    // vmcnt wait there would also drain the tiles' DMA).
+    drain_vector_loads();
 #pragma unroll
-    for (int k = 0; k < QK_STEPS; ++k) asm volatile("" : : "v"(qf[k]));
+    for (int k = 0; k < QK_STEPS; ++k) asm volatile("" : "+v"(qf[k]));
   }
 
   SegState st;
@@ -702,28 +789,34 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   // time: the empty asm keeps each block in AGPRs until its turn, so only 16
   // accumulators are copied to VGPRs at once.
   const float lsum = st.lsum + other_half(st.lsum);
-  if (!active || !valid) return true;
-  const int pl = w * PAIRS_WAVE + col;
-  uint16_t* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V;
+  if (!active) return true;
+  const int dh = w & 1;
 #pragma unroll
-  for (int d = 0; d < PV_BLOCKS; ++d) {
-    asm volatile("" : "+a"(st.acc[d]));
-    const f32x16 v = st.acc[d];
+  for (int j = 0; j < 2; ++j) {
+    const int pl = (w >> 1) * 2 * PAIRS_WAVE + j * PAIRS_WAVE + col;  // pair within the unit
+    const bool live = pb * PAIRS_BLOCK + pl < npairs;
+    uint16_t* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V + 256 * dh;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int dim = 32 * d + 8 * q4 + 4 * h;
-      u32x2 packed;
+    for (int d = 0; d < 8; ++d) {
+      asm volatile("" : "+a"(st.acc[2 * d + j]));
+      const f32x16 v = st.acc[2 * d + j];
+      if (!live) continue;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const __bf16 lo = (__bf16)v[4 * q4 + 2 * e];
-        const __bf16 hi = (__bf16)v[4 * q4 + 2 * e + 1];
-        packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dim = 32 * d + 8 * q4 + 4 * h;
+        u32x2 packed;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const __bf16 lo = (__bf16)v[4 * q4 + 2 * e];
+          const __bf16 hi = (__bf16)v[4 * q4 + 2 * e + 1];
+          packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *(u32x2*)(wo + dim) = packed;
       }
-      *(u32x2*)(wo + dim) = packed;
     }
   }
-  if (h == 0) {
-    float* ml = p.ws_ml + ((size_t)slot * PAIRS_BLOCK + pl) * 2;
+  if (h == 0 && valid) {
+    float* ml = p.ws_ml + ((size_t)slot * PAIRS_BLOCK + w * PAIRS_WAVE + col) * 2;
     ml[0] = st.m_ref;
     ml[1] = lsum;
   }
