@@ -184,7 +184,15 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* smem, uint32_t off)
 // Value of lane (l ^ 32): the two halves of a wave hold the two token halves of
 // the same pair.  (ds_bpermute; the permlane32_swap builtin applied to one value
 // twice has been folded incorrectly by the compiler.)
-__device__ __forceinline__ float other_half(float v) { return __shfl_xor(v, 32, 64); }
+// max / sum of a value over lanes l and l ^ 32 (v_permlane32_swap: no LDS trip)
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // 8 E4M3FN bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
 // Byte j of (lo, hi) becomes element j.  v_cvt_pk_f32_fp8 widens two codes to
@@ -480,9 +488,10 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 struct SegState {
   f32x16 acc[PV_BLOCKS];  // O^T accumulators: [2d + j] = dim block d of this wave's half, pair block j
   float m_ref;     // reference max, log2 units (identical in both lane halves)
-  float m_max;     // largest logit seen, log2 units
+  float m_max;     // largest logit of the masked-path tiles, log2 units (both halves)
+  float s_max;     // largest raw score of the fast-path tiles (this lane's tokens only)
   float lsum;      // this lane's share of the softmax denominator
-  bool over;       // some logit beat m_ref by more than the threshold
+  bool ref_ready;  // wave-uniform: every lane's m_ref is set
 };
 
 template <bool FP8, int PS, bool ACTIVE>
@@ -628,24 +637,34 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     // ---------------- softmax (exp2 domain); value k is token 16(k>>3) + 8h + (k&7)
     bf16x8 pc0, pc1;
     const int tok0 = t * TILE + 8 * h;
-    if (c_pos && (t + 1) * TILE <= min_vis) {
-      // every token of the tile is visible to every pair of this wave
-      float mx = s[0];
-#pragma unroll
-      for (int k = 1; k < 16; ++k) mx = fmaxf(mx, s[k]);
-      mx = fmaxf(mx, other_half(mx)) * c;
-      if (st.m_ref == -INFINITY) st.m_ref = mx;  // first visible tile sets the reference
-      st.m_max = fmaxf(st.m_max, mx);
-      st.over = st.over || (mx > st.m_ref + RESCALE_THRESHOLD);
+    if (c_pos && st.ref_ready && (t + 1) * TILE <= min_vis) {
+      // every token of the tile is visible to every pair of this wave and the
+      // reference is fixed: the exponentials depend on nothing but the scores;
+      // the running max only feeds the overflow check at the segment's end
       const float nm = -st.m_ref;
+      float e[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k], c, nm));
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c, nm));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 + j], c, nm));
-        st.lsum += e0 + e1;
-        pc0[j] = (__bf16)e0;
-        pc1[j] = (__bf16)e1;
+        pc0[j] = (__bf16)e[j];
+        pc1[j] = (__bf16)e[8 + j];
       }
+      float sum8[8], mx8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        sum8[k] = e[k] + e[8 + k];
+        mx8[k] = fmaxf(s[k], s[8 + k]);
+      }
+#pragma unroll
+      for (int n = 4; n >= 1; n >>= 1)
+#pragma unroll
+        for (int k = 0; k < n; ++k) {
+          sum8[k] += sum8[k + n];
+          mx8[k] = fmaxf(mx8[k], mx8[k + n]);
+        }
+      st.lsum += sum8[0];
+      st.s_max = fmaxf(st.s_max, mx8[0]);
     } else {
       float mx = -INFINITY;
 #pragma unroll
@@ -654,10 +673,9 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
         s[k] = v;
         mx = fmaxf(mx, v);
       }
-      mx = fmaxf(mx, other_half(mx));
-      if (st.m_ref == -INFINITY) st.m_ref = mx;
+      mx = max_halves(mx);
+      if (st.m_ref == -INFINITY) st.m_ref = mx;  // first tile with a visible token sets the reference
       st.m_max = fmaxf(st.m_max, mx);
-      st.over = st.over || (mx > st.m_ref + RESCALE_THRESHOLD);
       const float mbase = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -667,6 +685,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
         pc0[j] = (__bf16)e0;
         pc1[j] = (__bf16)e1;
       }
+      st.ref_ready = __builtin_amdgcn_ballot_w64(st.m_ref == -INFINITY) == 0;
     }
     // ---------------- P exchange: the partner wave (w ^ 1) owns the other 32 pairs
     // of this 64-pair group; each wave posts its P and reads the partner's
@@ -766,20 +785,26 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   for (int i = 0; i < PV_BLOCKS; ++i) st.acc[i] = f32x16{};
   st.m_ref = m_seed;
   st.m_max = m_seed;
+  st.s_max = -INFINITY;
   st.lsum = 0.f;
-  st.over = false;
+  st.ref_ready = __builtin_amdgcn_ballot_w64(m_seed == -INFINITY) == 0;
   if (active) segment_loop<FP8, PS, true>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
   else segment_loop<FP8, PS, false>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
 
-  // ---- segment end: all waves idle on LDS; one flag per wave says "redo"
+  // ---- segment end: the largest logit of the segment decides whether some
+  // exponential went past the threshold; all waves idle on LDS; one flag per
+  // wave says "redo"
+  const float fast_max = (st.s_max == -INFINITY) ? -INFINITY : max_halves(st.s_max) * p.scale_log2;
+  const float m_max = fmaxf(st.m_max, fast_max);
+  const bool over = m_max > st.m_ref + RESCALE_THRESHOLD;
   int* flags = (int*)(smem + FLAGS_OFF);
   wait_lgkm0();
   block_barrier();
-  if (lane == 0) flags[w] = __builtin_amdgcn_ballot_w64(st.over) != 0 ? 1 : 0;
+  if (lane == 0) flags[w] = __builtin_amdgcn_ballot_w64(over) != 0 ? 1 : 0;
   wait_lgkm0();
   block_barrier();
   if (uniform(flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
-    m_seed = st.m_max;
+    m_seed = m_max;
     return false;
   }
 
@@ -788,7 +813,7 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   // merge kernel divides by the summed denominator), one 32-dim block at a
   // time: the empty asm keeps each block in AGPRs until its turn, so only 16
   // accumulators are copied to VGPRs at once.
-  const float lsum = st.lsum + other_half(st.lsum);
+  const float lsum = sum_halves(st.lsum);
   if (!active) return true;
   const int dh = w & 1;
 #pragma unroll

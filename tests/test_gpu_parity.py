@@ -83,6 +83,42 @@ def test_forced_split_grid(grid):
     print("grid", grid, stats, flush=True)
 
 
+def _log2_logit_growth(w, b):
+    """Largest amount, in log2 units, by which a pair's logit over request b's
+    whole visible range beats its largest logit among the first 32 tokens."""
+    import math
+    r0 = int(w.qo_indptr[b]) if w.qo_indptr is not None else b * w.q_len_fixed
+    qb = int(w.q_lens()[b])
+    L = int(w.seq_lens[b])
+    ps = w.kv_bits.shape[1]
+    rows = w.kv_bits[w.block_tables[b, :(L + ps - 1) // ps]].reshape(-1, 576)[:L]
+    if w.kv_dtype == "bf16":
+        k = (rows.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        k = torch.from_numpy(rows).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    q = (w.q_bits[r0:r0 + qb].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    s = np.einsum("rhd,td->rht", q, k) * w.bmm1_scale / math.log(2.0)
+    growth = -np.inf
+    for qi in range(qb):
+        vis = L - qb + qi + 1 if w.causal else L
+        growth = max(growth, float((s[qi, :, :vis].max(axis=1) - s[qi, :, :min(vis, 32)].max(axis=1)).max()))
+    return growth
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("grid", [1, 8])
+def test_reference_restart(kv_dtype, grid):
+    """Unscaled logits (bmm1_scale 1) make later tokens beat the first tile's
+    max by far more than 2^32: segments have to be redone with the observed
+    max as the reference, and must still match the oracle."""
+    w = make_workload("restart", seed=21, batch=3, seq_len_range=(600, 2000), num_heads=32, q_len=2,
+                      page_size=32, kv_dtype=kv_dtype, bmm1_scale=1.0, causal=True, want_lse=True)
+    assert max(_log2_logit_growth(w, b) for b in range(w.batch)) > 40.0
+    binding.set_grid_override(grid)
+    stats = compare_with_oracle(w)
+    print("restart", kv_dtype, grid, stats, flush=True)
+
+
 def test_deterministic_and_permutation_invariant():
     w = named_workload("tiny_bf16")
     o1, l1 = run_hip(w)
