@@ -76,6 +76,7 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_THRESHOLD = 32.0f;
 
 static_assert(LDS_BYTES <= 163840, "LDS budget");
+static_assert(PAIRS_BLOCK * D_V * 2 <= NBUF * TILEB, "the O block is staged in the tile buffers");
 static_assert(SCAN_SCRATCH_OFF + 2 * THREADS * 4 <= TILEB, "plan scratch fits in one tile buffer");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -181,10 +182,9 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* smem, uint32_t off)
       (__attribute__((address_space(3))) i32x2*)((__attribute__((address_space(3))) uint8_t*)smem + off));
 }
 
-// Value of lane (l ^ 32): the two halves of a wave hold the two token halves of
-// the same pair.  (ds_bpermute; the permlane32_swap builtin applied to one value
-// twice has been folded incorrectly by the compiler.)
-// max / sum of a value over lanes l and l ^ 32 (v_permlane32_swap: no LDS trip)
+// Max / sum of a value over lanes l and l ^ 32, which hold the two token halves
+// of the same pair.  v_permlane32_swap on two copies of the value leaves lane l
+// of one copy and lane l ^ 32 of the other in lane l: no LDS round trip.
 __device__ __forceinline__ float max_halves(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -808,35 +808,38 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
     return false;
   }
 
-  // ---------------- epilogue: the two lane halves hold the two token halves.
-  // O goes out unnormalised as bf16 (its scale is relative to m_ref, and the
-  // merge kernel divides by the summed denominator), one 32-dim block at a
-  // time: the empty asm keeps each block in AGPRs until its turn, so only 16
-  // accumulators are copied to VGPRs at once.
+  // ---------------- epilogue.  O goes out unnormalised as bf16 (its scale is
+  // relative to m_ref; the merge kernel divides by the summed denominator).
+  // It is staged in LDS (the tile buffers are all consumed) as the unit's
+  // [128 pairs][512 dims] block, 16-byte chunk c of row r at chunk c ^ (r & 15),
+  // so that each wave then stores whole 1 KB rows.  The accumulators go out one
+  // 32-dim block at a time: the empty asm keeps each block in AGPRs until its
+  // turn, so only 16 of them are copied to VGPRs at once.
   const float lsum = sum_halves(st.lsum);
-  if (!active) return true;
-  const int dh = w & 1;
+  if (active) {
+    const int dh = w & 1;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int pl = (w >> 1) * 2 * PAIRS_WAVE + j * PAIRS_WAVE + col;  // pair within the unit
-    const bool live = pb * PAIRS_BLOCK + pl < npairs;
-    uint16_t* wo = p.ws_o + ((size_t)slot * PAIRS_BLOCK + pl) * D_V + 256 * dh;
+    for (int j = 0; j < 2; ++j) {
+      const int r = (w >> 1) * 2 * PAIRS_WAVE + j * PAIRS_WAVE + col;  // pair within the unit
+      const uint32_t rowb = (uint32_t)r * (D_V * 2) + 8 * h;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      asm volatile("" : "+a"(st.acc[2 * d + j]));
-      const f32x16 v = st.acc[2 * d + j];
-      if (!live) continue;
+      for (int d = 0; d < 8; ++d) {
+        asm volatile("" : "+a"(st.acc[2 * d + j]));
+        const f32x16 v = st.acc[2 * d + j];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dim = 32 * d + 8 * q4 + 4 * h;
-        u32x2 packed;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          // lane holds dims 256 dh + 32 d + 8 q4 + 4 h .. +4: chunk 32 dh + 4 d + q4
+          const int chunk = 32 * dh + 4 * d + q4;
+          u32x2 packed;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const __bf16 lo = (__bf16)v[4 * q4 + 2 * e];
-          const __bf16 hi = (__bf16)v[4 * q4 + 2 * e + 1];
-          packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          for (int e = 0; e < 2; ++e) {
+            const __bf16 lo = (__bf16)v[4 * q4 + 2 * e];
+            const __bf16 hi = (__bf16)v[4 * q4 + 2 * e + 1];
+            packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          *(__attribute__((address_space(3))) u32x2*)((__attribute__((address_space(3))) uint8_t*)smem + rowb +
+                                                     16 * (chunk ^ (r & 15))) = packed;
         }
-        *(u32x2*)(wo + dim) = packed;
       }
     }
   }
@@ -845,6 +848,26 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
     ml[0] = st.m_ref;
     ml[1] = lsum;
   }
+  wait_lgkm0();
+  block_barrier();  // the O block is in LDS
+  // wave w stores rows [32 w, 32 w + 32), eight at a time, 16 bytes per lane
+  uint16_t* wo = p.ws_o + (size_t)slot * PAIRS_BLOCK * D_V + 8 * lane;
+#pragma unroll
+  for (int r8 = 0; r8 < PAIRS_WAVE; r8 += 8) {
+    u32x4 rows[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = w * PAIRS_WAVE + r8 + i;
+      rows[i] = lds_read_b128(smem, (uint32_t)r * (D_V * 2) + 16 * (lane ^ (r & 15)));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = w * PAIRS_WAVE + r8 + i;
+      if (pb * PAIRS_BLOCK + r < npairs) *(u32x4*)(wo + (size_t)r * D_V) = rows[i];
+    }
+  }
+  wait_lgkm0();
+  block_barrier();  // LDS is free for the next segment's tiles
   return true;
 }
 
