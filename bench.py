@@ -201,8 +201,9 @@ def run_workload(name, steps, warmup, want_cpu):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: the GPU reaches steady clocks only after tens of ms of work")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads (lines on stderr)")

@@ -135,6 +135,18 @@ const char* mla_status_string(int status);
 void mla_decode_internal_set_grid_override(int32_t grid);
 
 /*
+ * Tuning hook, not part of the serving interface: the work split gives every
+ * workgroup an equal share of (tiles + segment starts x cost), where a segment
+ * is one workgroup's contiguous run of 32-row KV tiles of one 128-pair unit and
+ * its start (query load, first tiles in flight, partial-output store) is
+ * charged `tiles` tile-equivalents.  Negative restores the default (8); values
+ * are capped at 256.  Changes how KV ranges are split and merged, never the
+ * result beyond rounding.  Affects later calls on every device; not thread-safe
+ * against concurrent launches.
+ */
+void mla_decode_internal_set_segment_cost(int32_t tiles);
+
+/*
  * Measurement hook, not part of the serving interface: when both are non-NULL,
  * later mla_decode_paged calls record start_event (a hipEvent_t) on their stream
  * right before the decode kernel and stop_event right after it, before the split

@@ -64,6 +64,8 @@ def load_library():
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_decode_internal_set_grid_override.argtypes = [i32]
     lib.mla_decode_internal_set_grid_override.restype = None
+    lib.mla_decode_internal_set_segment_cost.argtypes = [i32]
+    lib.mla_decode_internal_set_segment_cost.restype = None
     lib.mla_decode_internal_set_kernel_events.argtypes = [vp, vp]
     lib.mla_decode_internal_set_kernel_events.restype = None
     lib.mla_decode_internal_fp8_to_bf16.argtypes = [vp, vp, i64, vp]
@@ -109,6 +111,12 @@ def mla_decode_paged(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len
 def set_grid_override(grid):
     """Test hook: force the persistent grid size (0 = one workgroup per CU)."""
     load_library().mla_decode_internal_set_grid_override(int(grid))
+
+
+def set_segment_cost(tiles):
+    """Tuning hook: the work split's cost of a segment start, in tiles
+    (negative restores the default)."""
+    load_library().mla_decode_internal_set_segment_cost(int(tiles))
 
 
 def set_kernel_events(start_event, stop_event):

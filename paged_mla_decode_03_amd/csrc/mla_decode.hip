@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -74,6 +75,10 @@ constexpr float LN2 = 0.6931471805599453f;
 // A segment is redone with a raised reference max only when a logit beats the
 // reference by more than 2^32: P and the fp32 sums stay far from overflow below.
 constexpr float RESCALE_THRESHOLD = 32.0f;
+// Work-split cost of a segment's start (query load, first tiles, O store) in
+// tile-equivalents; the split balances tiles plus this per segment.
+constexpr int SEG_COST_DEFAULT = 8;
+constexpr int SEG_COST_MAX = 256;
 
 static_assert(LDS_BYTES <= 163840, "LDS budget");
 static_assert(PAIRS_BLOCK * D_V * 2 <= NBUF * TILEB, "the O block is staged in the tile buffers");
@@ -97,7 +102,7 @@ struct Params {
   float* lse;
   uint16_t* ws_o;   // [G + U][128][512] bf16 O per segment (unnormalised)
   float* ws_ml;     // [G + U][128][2]   per segment (max in log2 units, sum)
-  int32_t* ws_plan; // [0] = tiles per workgroup C, [1] = total tiles,
+  int32_t* ws_plan; // [0] = cost per workgroup C, [1] = total cost,
                     // [2 + b] = tile offset of request b (b <= B),
                     // [3 + B + b] = first global unit of request b (b <= B)
   int32_t batch;
@@ -109,6 +114,7 @@ struct Params {
   float scale_log2;  // bmm1_scale * log2(e)
   float bmm2;
   int32_t causal;
+  int32_t seg_cost;  // cost of starting a segment, in tiles (see the work plan)
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -274,6 +280,11 @@ __device__ __forceinline__ void lds_zero16(uint8_t* smem, uint32_t off) {
 // tile_off[b] = first linear tile of request b, tile_off[B] = total tiles;
 // unit_off[b] = first global unit of request b, unit_off[B] = total units.
 // A request contributes ceil(q_b*H / 128) units of ceil(L_b / 32) tiles each.
+// 128-pair units and 32-row tiles of request b (lengths outside the documented
+// ranges count as empty, so that the work walk always advances)
+__device__ __forceinline__ int request_units(const Params& p, int qb) { return max(0, ceil_div(qb * p.heads, PAIRS_BLOCK)); }
+__device__ __forceinline__ int request_tiles(const Params& p, int b) { return max(0, ceil_div(p.seq_lens[b], TILE)); }
+
 __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* scan) {
   const int tid = threadIdx.x;
   const int B = p.batch;
@@ -284,9 +295,9 @@ __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* s
   for (int b = b0; b < b1; ++b) {
     int r0;
     const int qb = request_rows(p, b, r0);
-    const int u = ceil_div(qb * p.heads, PAIRS_BLOCK);
+    const int u = request_units(p, qb);
     units += u;
-    tiles += u * ceil_div(p.seq_lens[b], TILE);
+    tiles += u * request_tiles(p, b);
   }
   int* scan_t = scan;
   int* scan_u = scan + THREADS;
@@ -306,10 +317,10 @@ __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* s
   for (int b = b0; b < b1; ++b) {
     int r0;
     const int qb = request_rows(p, b, r0);
-    const int u = ceil_div(qb * p.heads, PAIRS_BLOCK);
+    const int u = request_units(p, qb);
     tile_off[b] = run_t;
     unit_off[b] = run_u;
-    run_t += u * ceil_div(p.seq_lens[b], TILE);
+    run_t += u * request_tiles(p, b);
     run_u += u;
   }
   if (tid == THREADS - 1) {
@@ -882,9 +893,14 @@ void mla_decode_kernel(Params p) {
   int* unit_off = (int*)(smem + UNIT_SCRATCH_OFF);
   build_plan(p, tile_off, unit_off, (int*)(smem + SCAN_SCRATCH_OFF));
   const int B = p.batch;
-  const int TT = uniform(tile_off[B]);
+  const int S0 = p.seg_cost;
+  // Cost space: unit u (request b, pair block pb) takes S0 + T_b consecutive
+  // positions, S0 for the segment start it forces and then one per tile, so
+  // tile t of u sits at tile_off[b] + pb T_b + t + (u + 1) S0.  Workgroup g takes
+  // the positions [g C, (g + 1) C): equal cost, counting each extra segment.
+  const int TC = uniform(tile_off[B] + unit_off[B] * S0);
   const int G = p.grid;
-  const int C = max(1, ceil_div(TT, G));
+  const int C = max(1, ceil_div(TC, G));
   if (blockIdx.x == 0) {
     for (int b = threadIdx.x; b <= B; b += THREADS) {
       p.ws_plan[2 + b] = tile_off[b];
@@ -892,7 +908,7 @@ void mla_decode_kernel(Params p) {
     }
     if (threadIdx.x == 0) {
       p.ws_plan[0] = C;
-      p.ws_plan[1] = TT;
+      p.ws_plan[1] = TC;
     }
   }
   // Consecutive logical workgroups sit on one XCD (dispatch is round-robin over
@@ -900,30 +916,45 @@ void mla_decode_kernel(Params p) {
   const int i = blockIdx.x;
   const int g = (G % 8 == 0) ? ((i & 7) * (G >> 3) + (i >> 3)) : i;
   int x = g * C;
-  const int end = min(TT, x + C);
+  const int end = min(TC, x + C);
   int b = 0, rel = 0;
   if (x < end) {
-    int lo = 0, hi = B;  // tile_off[lo] <= x < tile_off[hi]
+    int lo = 0, hi = B;  // cost offset of request lo <= x < that of request hi
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (tile_off[mid] <= x) lo = mid; else hi = mid;
+      if (tile_off[mid] + unit_off[mid] * S0 <= x) lo = mid; else hi = mid;
     }
     b = lo;
-    rel = x - tile_off[lo];
+    rel = x - (tile_off[lo] + unit_off[lo] * S0);
   }
   b = uniform(b);
   rel = uniform(rel);
   int u_base = uniform(unit_off[b]);  // global unit index of request b's first unit
   __syncthreads();  // the LDS plan is dead from here on
   while (x < end) {
-    // walk the linear (unit, tile) space forward from request b
+    // walk the cost space forward from request b
     const int L = uniform(p.seq_lens[b]);
     int r0;
     const int qb = uniform(request_rows(p, b, r0));
-    const int T = ceil_div(L, TILE);
-    const int units = ceil_div(qb * p.heads, PAIRS_BLOCK);
-    const int pb = rel / T;
-    const int t0 = rel - pb * T;
+    const int T = uniform(request_tiles(p, b));
+    const int units = uniform(request_units(p, qb));
+    const int span = S0 + T;
+    if (T == 0 || units == 0) {  // nothing to compute (lengths outside the contract)
+      x += units * S0 - rel;
+      rel = 0;
+      ++b;
+      u_base += units;
+      continue;
+    }
+    const int pb = rel / span;
+    int r = rel - pb * span;
+    if (r < S0) {  // a unit's start: its tiles begin S0 - r positions on
+      x += S0 - r;
+      rel += S0 - r;
+      r = S0;
+      if (x >= end) break;
+    }
+    const int t0 = r - S0;
     const int t1 = min(T, t0 + (end - x));
     // segment (workgroup g, global unit u) has slot g + u: unique, since every
     // later segment has a larger g or a larger u
@@ -933,7 +964,7 @@ void mla_decode_kernel(Params p) {
     }
     x += t1 - t0;
     rel += t1 - t0;
-    if (rel >= units * T) {
+    if (rel >= units * span) {
       ++b;
       rel = 0;
       u_base += units;
@@ -972,8 +1003,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int pl = pair - pb * PAIRS_BLOCK;
   const int C = p.ws_plan[0];
   const int T = ceil_div(p.seq_lens[b], TILE);
-  const int U0 = p.ws_plan[2 + b] + pb * T;
   const int u = p.ws_plan[3 + p.batch + b] + pb;
+  const int U0 = p.ws_plan[2 + b] + pb * T + (u + 1) * p.seg_cost;  // cost position of the unit's first tile
   const int g0 = U0 / C;
   const int g1 = (U0 + T - 1) / C;
   float M = -INFINITY;
@@ -1020,6 +1051,7 @@ __global__ void fp8_to_bf16_kernel(const u32x2* in, bf16x8* out, int64_t n) {
 constexpr int MAX_DEVICES = 64;
 std::atomic<int> g_cu_count[MAX_DEVICES];
 std::atomic<int> g_grid_override{0};
+std::atomic<int> g_seg_cost{SEG_COST_DEFAULT};
 std::atomic<void*> g_ev_start{nullptr};
 std::atomic<void*> g_ev_stop{nullptr};
 
@@ -1069,8 +1101,9 @@ int validate(const mla_decode_dims_t* d, int32_t max_seq_len, int32_t max_q_len,
     return MLA_ERR_BAD_Q_LEN;
   if (packed && d->total_q > (int64_t)d->batch * max_q_len) return MLA_ERR_BAD_Q_LEN;
   if ((int64_t)d->block_table_stride * d->page_size < max_seq_len) return MLA_ERR_BAD_BLOCK_TABLE;
-  // 32-bit tile arithmetic on device
-  if (max_units(d, max_q_len) * ((max_seq_len + TILE - 1) / TILE) >= (int64_t)1 << 30) return MLA_ERR_BAD_SHAPE;
+  // 32-bit cost arithmetic on device
+  if (max_units(d, max_q_len) * ((max_seq_len + TILE - 1) / TILE + SEG_COST_MAX) >= (int64_t)1 << 30)
+    return MLA_ERR_BAD_SHAPE;
   return MLA_OK;
 }
 
@@ -1148,6 +1181,7 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
   p.scale_log2 = bmm1_scale * LOG2E;
   p.bmm2 = bmm2_scale;
   p.causal = causal ? 1 : 0;
+  p.seg_cost = g_seg_cost.load(std::memory_order_relaxed);
 
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = dims->kv_dtype == MLA_KV_FP8_E4M3FN;
@@ -1167,6 +1201,10 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
 }
 
 void mla_decode_internal_set_grid_override(int32_t grid) { g_grid_override.store(grid > 0 ? grid : 0); }
+
+void mla_decode_internal_set_segment_cost(int32_t tiles) {
+  g_seg_cost.store(tiles < 0 ? SEG_COST_DEFAULT : std::min(tiles, SEG_COST_MAX));
+}
 
 void mla_decode_internal_set_kernel_events(void* start_event, void* stop_event) {
   g_ev_start.store(start_event);

@@ -21,8 +21,10 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True)
 def _default_grid():
     binding.set_grid_override(0)
+    binding.set_segment_cost(-1)
     yield
     binding.set_grid_override(0)
+    binding.set_segment_cost(-1)
 
 
 def test_tiny_bf16_full():
@@ -117,6 +119,19 @@ def test_reference_restart(kv_dtype, grid):
     binding.set_grid_override(grid)
     stats = compare_with_oracle(w)
     print("restart", kv_dtype, grid, stats, flush=True)
+
+
+@pytest.mark.parametrize("cost", [0, 3, 40, 256])
+@pytest.mark.parametrize("grid", [8, 64])
+def test_segment_cost_split(cost, grid):
+    """The split's per-segment cost moves segment boundaries (and can leave
+    workgroups with no tiles at all); every split must match the oracle."""
+    binding.set_grid_override(grid)
+    binding.set_segment_cost(cost)
+    w = make_workload("segcost", seed=8, batch=4, seq_len_range=(40, 1200), num_heads=64, q_len=3, page_size=32,
+                      bmm1_scale=INV_SQRT_192, causal=True, want_lse=True)
+    stats = compare_with_oracle(w)
+    print("segment cost", cost, "grid", grid, stats, flush=True)
 
 
 def test_deterministic_and_permutation_invariant():
