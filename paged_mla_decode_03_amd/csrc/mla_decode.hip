@@ -497,7 +497,7 @@ __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint3
 
 // Per-lane state of an active wave.
 struct SegState {
-  f32x16 acc[PV_BLOCKS];  // O^T accumulators: [2d + j] = dim block d of this wave's half, pair block j
+  f32x16 acc[PV_BLOCKS];  // O^T accumulators: [2d] own pairs, [2d + 1] the partner's; dim block d of the half
   float m_ref;     // reference max, log2 units (identical in both lane halves)
   float m_max;     // largest logit of the masked-path tiles, log2 units (both halves)
   float s_max;     // largest raw score of the fast-path tiles (this lane's tokens only)
@@ -555,7 +555,6 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   //   fp8  A : base | 16 qs (bits 4..7), step kk: ^ 16 kk
   //   fp8  V : base | 16 (g1 ^ (8h + tr_z)) (bits 4..7) + 256 dh, block d: ^ 32 d, + 8192c
   const uint32_t a_lane = FP8 ? qa_lat + 16 * qs_lat : qa_lat + 32 * qs_lat;
-  const int sub = w & 1;  // which 32 pairs of the 64-pair group this wave's QK^T covers
   const uint32_t ps_own = PSLOT_OFF + w * PSLOT_BYTES + lane * 16;
   const uint32_t ps_other = PSLOT_OFF + (w ^ 1) * PSLOT_BYTES + lane * 16;
   const int dh = w & 1;  // P.V output half: dims [256 dh, 256 dh + 256)
@@ -598,9 +597,10 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   auto to_bf16 = [&](const u32x4& raw) -> bf16x8 {
     return FP8 ? fp8x8_to_bf16x8(raw[0], raw[1]) : __builtin_bit_cast(bf16x8, raw);
   };
-  // QK^T of the tile in buf; the DMA instructions of the pending tile load go
-  // out one every four MFMAs
-  auto qk = [&](uint32_t buf_in, const TileLoad& tl) -> f32x16 {
+  // QK^T of the tile in buf.  fill(k) runs right after MFMA k: independent VALU
+  // work (the previous tile's softmax) that the wave issues while the matrix
+  // core is busy; the scheduling barrier keeps each piece in its slot.
+  auto qk = [&](uint32_t buf_in, auto&& fill) -> f32x16 {
     const uint32_t buf = opaque(buf_in);
     f32x16 s;
     constexpr int GA = 4;  // A fragments read this many steps ahead
@@ -613,11 +613,13 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       if (k + GA < QK_STEPS) araw[k % GA] = load_a(buf, k + GA);
       if (k == 0) s = mfma_first_vgpr(to_bf16(cur), qf[k]);
       else mfma_acc_vgpr(s, to_bf16(cur), qf[k]);
-      if ((k & 3) == 3 && (k >> 2) < LOADS) issue_tile_part<FP8>(tl, k >> 2);
+      fill(k);
+      __builtin_amdgcn_sched_barrier(0);
     }
     mfma_fence(s);
     return s;
   };
+  auto no_fill = [](int) {};
 
   // Tile t has landed once at most the DMA ops of the n tiles issued after it
   // remain; a partial tile among them makes the count unknown, so drain.
@@ -631,75 +633,121 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   const float c = p.scale_log2;
   const bool c_pos = c > 0.f;
 
-  for (int t = t0; t < t1; ++t) {
-    wait_tile(t, 2);
-    wait_lgkm0();
-    block_barrier();  // tile t is in LDS; tile t-1's buffer is free
-    TileLoad tl{nullptr, 0u, 0u};
-    if (t + 3 < t1) tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
-    if (!ACTIVE) {
+  // ---------------- softmax (exp2 domain) of one tile's scores s; value k is
+  // token 16(k>>3) + 8h + (k&7) of the tile.
+  // Fast path (every token of the tile visible to every pair of this wave, the
+  // reference fixed): the exponentials depend on nothing but the scores, and
+  // the running max only feeds the overflow check at the segment's end.  It is
+  // cut into QK_STEPS pieces so that it can sit between the next tile's MFMAs.
+  // Pieces 4m .. 4m+3 handle tokens j, j+1 of both lane halves' 8-token runs
+  // (j = 2m): two exponentials, two more, the bf16 packing, the running sum and
+  // max; piece 16 folds them into the segment state.  Few values are live at once.
+  float e[4], run_sum = 0.f, run_mx = -INFINITY;
+  bf16x8 pc0, pc1;
+  auto fast_piece = [&](const f32x16& s, float nm, int k) {
+    const int j = 2 * (k >> 2);
+    switch (k < 16 ? (k & 3) : 4) {
+      case 0:
+        e[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c, nm));
+        e[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j + 1], c, nm));
+        break;
+      case 1:
+        e[2] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 + j], c, nm));
+        e[3] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[9 + j], c, nm));
+        break;
+      case 2:
+        pc0[j] = (__bf16)e[0];
+        pc0[j + 1] = (__bf16)e[1];
+        pc1[j] = (__bf16)e[2];
+        pc1[j + 1] = (__bf16)e[3];
+        break;
+      case 3: {
+        const float sm = (e[0] + e[1]) + (e[2] + e[3]);
+        const float mx = fmaxf(fmaxf(s[j], s[j + 1]), fmaxf(s[8 + j], s[9 + j]));
+        run_sum = (j == 0) ? sm : run_sum + sm;
+        run_mx = (j == 0) ? mx : fmaxf(run_mx, mx);
+        break;
+      }
+      default:
+        if (k == 16) {
+          st.lsum += run_sum;
+          st.s_max = fmaxf(st.s_max, run_mx);
+        }
+        break;
+    }
+  };
+  // Masked path: causal edge tiles, and the first tile (which sets the reference).
+  auto masked_softmax = [&](f32x16 s, int t) {
+    const int tok0 = t * TILE + 8 * h;
+    float mx = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < LOADS; ++k) issue_tile_part<FP8>(tl, k);
+    for (int k = 0; k < 16; ++k) {
+      const float v = (tok0 + 16 * (k >> 3) + (k & 7)) < n_vis ? s[k] * c : -INFINITY;
+      s[k] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = max_halves(mx);
+    if (st.m_ref == -INFINITY) st.m_ref = mx;  // first tile with a visible token sets the reference
+    st.m_max = fmaxf(st.m_max, mx);
+    const float mbase = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e0 = __builtin_amdgcn_exp2f(s[j] - mbase);
+      const float e1 = __builtin_amdgcn_exp2f(s[8 + j] - mbase);
+      st.lsum += e0 + e1;
+      pc0[j] = (__bf16)e0;
+      pc1[j] = (__bf16)e1;
+    }
+    st.ref_ready = __builtin_amdgcn_ballot_w64(st.m_ref == -INFINITY) == 0;
+  };
+
+  // The loop runs one tile ahead in QK^T: iteration t computes QK^T of tile t+1
+  // with tile t's softmax between its MFMAs, exchanges P of tile t, then does
+  // P.V of tile t.  Tiles t0 .. t0+2 are in flight on entry.
+  wait_tile(t0, 2);
+  wait_lgkm0();
+  block_barrier();  // tile t0 is in LDS
+  f32x16 s_next{};
+  if (ACTIVE) s_next = qk(buf_of(t0), no_fill);
+  for (int t = t0; t < t1; ++t) {
+    const f32x16 s = s_next;
+    const bool fast = c_pos && st.ref_ready && (t + 1) * TILE <= min_vis;
+    if (t + 1 < t1) {
+      wait_tile(t + 1, 1);
+      wait_lgkm0();
+      block_barrier();  // tile t+1 is in LDS; every wave is done with tile t-1's buffer
+      if (t + 3 < t1) issue_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
+      if (ACTIVE) {
+        if (fast) {
+          const float nm = -st.m_ref;
+          s_next = qk(buf_of(t + 1), [&](int k) { fast_piece(s, nm, k); });
+        } else {
+          masked_softmax(s, t);
+          s_next = qk(buf_of(t + 1), no_fill);
+        }
+      }
+    } else if (ACTIVE) {
+      if (fast) {
+        const float nm = -st.m_ref;
+#pragma unroll
+        for (int k = 0; k < QK_STEPS; ++k) fast_piece(s, nm, k);
+      } else {
+        masked_softmax(s, t);
+      }
+    }
+    if (!ACTIVE) {
       wait_lgkm0();
       block_barrier();  // P of tile t posted
       continue;
     }
-    f32x16 s = qk(buf_of(t), tl);
-    // ---------------- softmax (exp2 domain); value k is token 16(k>>3) + 8h + (k&7)
-    bf16x8 pc0, pc1;
-    const int tok0 = t * TILE + 8 * h;
-    if (c_pos && st.ref_ready && (t + 1) * TILE <= min_vis) {
-      // every token of the tile is visible to every pair of this wave and the
-      // reference is fixed: the exponentials depend on nothing but the scores;
-      // the running max only feeds the overflow check at the segment's end
-      const float nm = -st.m_ref;
-      float e[16];
+    // ---------------- P exchange: the partner wave (w ^ 1) owns the other 32
+    // pairs of this 64-pair group; each wave posts its P and reads the
+    // partner's.  The first V^T fragments are read across the barrier.
+    const uint32_t buf = opaque(buf_of(t));
+    constexpr int GV = 4;  // V^T fragments read this many steps ahead
+    u32x4 vraw[GV];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) e[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k], c, nm));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pc0[j] = (__bf16)e[j];
-        pc1[j] = (__bf16)e[8 + j];
-      }
-      float sum8[8], mx8[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        sum8[k] = e[k] + e[8 + k];
-        mx8[k] = fmaxf(s[k], s[8 + k]);
-      }
-#pragma unroll
-      for (int n = 4; n >= 1; n >>= 1)
-#pragma unroll
-        for (int k = 0; k < n; ++k) {
-          sum8[k] += sum8[k + n];
-          mx8[k] = fmaxf(mx8[k], mx8[k + n]);
-        }
-      st.lsum += sum8[0];
-      st.s_max = fmaxf(st.s_max, mx8[0]);
-    } else {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float v = (tok0 + 16 * (k >> 3) + (k & 7)) < n_vis ? s[k] * c : -INFINITY;
-        s[k] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = max_halves(mx);
-      if (st.m_ref == -INFINITY) st.m_ref = mx;  // first tile with a visible token sets the reference
-      st.m_max = fmaxf(st.m_max, mx);
-      const float mbase = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e0 = __builtin_amdgcn_exp2f(s[j] - mbase);
-        const float e1 = __builtin_amdgcn_exp2f(s[8 + j] - mbase);
-        st.lsum += e0 + e1;
-        pc0[j] = (__bf16)e0;
-        pc1[j] = (__bf16)e1;
-      }
-      st.ref_ready = __builtin_amdgcn_ballot_w64(st.m_ref == -INFINITY) == 0;
-    }
-    // ---------------- P exchange: the partner wave (w ^ 1) owns the other 32 pairs
-    // of this 64-pair group; each wave posts its P and reads the partner's
+    for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
     *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own) = pc0;
     *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own + 1024) =
         pc1;
@@ -709,30 +757,24 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
         (const __attribute__((address_space(3))) uint8_t*)smem + ps_other);
     const bf16x8 pp1 = *(const __attribute__((address_space(3))) bf16x8*)(
         (const __attribute__((address_space(3))) uint8_t*)smem + ps_other + 1024);
-    // pair block j of the group: j == sub is this wave's own P
-    const bf16x8 b00 = sub ? pp0 : pc0, b01 = sub ? pp1 : pc1;  // block 0, chunks 0 / 1
-    const bf16x8 b10 = sub ? pc0 : pp0, b11 = sub ? pc1 : pp1;  // block 1
-    // ---------------- O^T (this wave's 256 dims, both pair blocks) += V^T . P^T:
-    // each V^T fragment feeds two MFMAs
-    {
-      const uint32_t buf = opaque(buf_of(t));
-      constexpr int GV = 4;  // V^T fragments read this many steps ahead
-      u32x4 vraw[GV];
+    // ---------------- O^T (this wave's 256 dims) += V^T . P^T for the wave's own
+    // 32 pairs (acc[2d]) and the partner's (acc[2d + 1]): each V^T fragment
+    // feeds two MFMAs.  The own-P MFMAs of the first GV steps go first, while
+    // the partner's P is still on its way.
 #pragma unroll
-      for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
+    for (int step = 0; step < GV; ++step)
+      mfma_acc_agpr(st.acc[2 * (step & 7)], to_bf16(vraw[step]), pc0);
 #pragma unroll
-      for (int step = 0; step < PV_BLOCKS; ++step) {
-        const u32x4 cur = vraw[step % GV];
-        if (step + GV < PV_BLOCKS) vraw[step % GV] = load_v(buf, step + GV);
-        const int d = step & 7;
-        const bf16x8 v = to_bf16(cur);
-        mfma_acc_agpr(st.acc[2 * d], v, (step >> 3) ? b01 : b00);
-        mfma_acc_agpr(st.acc[2 * d + 1], v, (step >> 3) ? b11 : b10);
-      }
-      // results land before anything but the next tile's MFMAs can touch them
-      // (the compiler may copy the accumulators once the loop exits)
-      asm volatile("s_nop 7\n\ts_nop 3" ::: "memory");
+    for (int step = 0; step < PV_BLOCKS; ++step) {
+      const int d = step & 7;
+      const bf16x8 v = to_bf16(vraw[step % GV]);
+      if (step >= GV) mfma_acc_agpr(st.acc[2 * d], v, (step >> 3) ? pc1 : pc0);
+      mfma_acc_agpr(st.acc[2 * d + 1], v, (step >> 3) ? pp1 : pp0);
+      if (step + GV < PV_BLOCKS) vraw[step % GV] = load_v(buf, step + GV);
     }
+    // results land before anything but the next tile's MFMAs can touch them
+    // (the compiler may copy the accumulators once the loop exits)
+    asm volatile("s_nop 7\n\ts_nop 3" ::: "memory");
   }
 }
 
@@ -831,7 +873,8 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
     const int dh = w & 1;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int r = (w >> 1) * 2 * PAIRS_WAVE + j * PAIRS_WAVE + col;  // pair within the unit
+      // acc[2d] holds this wave's own 32 pairs, acc[2d + 1] its partner's
+      const int r = (w >> 1) * 2 * PAIRS_WAVE + (j ^ (w & 1)) * PAIRS_WAVE + col;  // pair within the unit
       const uint32_t rowb = (uint32_t)r * (D_V * 2) + 8 * h;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
