@@ -271,8 +271,14 @@ __device__ __forceinline__ constexpr int swz_lat_fp8(int row) { return row & 15;
 __device__ __forceinline__ constexpr int swz_rope_fp8(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ void lds_zero16(uint8_t* smem, uint32_t off) {
+  // zeros made in place (a zero vector kept live across the loop only gets spilled)
+  uint32_t z0, z1, z2, z3;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z1));
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z2));
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z3));
   *(__attribute__((address_space(3))) u32x4*)((__attribute__((address_space(3))) uint8_t*)smem + off) =
-      u32x4{0, 0, 0, 0};
+      u32x4{z0, z1, z2, z3};
 }
 
 // ---------------------------------------------------------------- work plan
@@ -332,9 +338,11 @@ __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* s
 
 // ---------------------------------------------------------------- page-id window
 //
-// A segment's block-table entries are read once, 128 at a time, into two
-// VGPRs (lane i holds entries base + i and base + 64 + i); each tile's page id
-// is then a v_readlane, so issuing a tile's loads never waits on memory.
+// A segment's block-table entries are read once, WIN (128 or 64) at a time,
+// into one or two VGPRs (lane i holds entries base + i and base + 64 + i); each
+// tile's page id is then a v_readlane, so issuing a tile's loads never waits on
+// memory.  The fp8 kernels keep a 64-entry window: their tile loop has no
+// register to spare for the second one.
 struct PageWin {
   int base;  // first block-table index held (wave-uniform)
   int lo;    // entry base + lane
@@ -342,12 +350,13 @@ struct PageWin {
 };
 
 // Entries past the request's last page are never read (they may be garbage).
+template <int WIN>
 __device__ __forceinline__ void load_page_window(const Params& p, int b, int npages, int base, PageWin& pw) {
   const int lane = threadIdx.x & 63;
   const int32_t* row = p.block_tables + (size_t)b * p.bt_stride;
   pw.base = base;
   pw.lo = (base + lane < npages) ? row[base + lane] : 0;
-  pw.hi = (base + 64 + lane < npages) ? row[base + 64 + lane] : 0;
+  pw.hi = (WIN > 64 && base + 64 + lane < npages) ? row[base + 64 + lane] : 0;
   drain_vector_loads();
 }
 
@@ -355,17 +364,21 @@ __device__ __forceinline__ void load_page_window(const Params& p, int b, int npa
 
 // Page id of cache row `row` (< L) of request b, from the window (refilled when
 // the row's page lies past it: drain the loads in flight so the refill is the
-// only vector load the following waits can see, then read the next 128).
-template <int PS>
+// only vector load the following waits can see, then read the next WIN).
+template <int PS, int WIN>
 __device__ __forceinline__ int page_id(const Params& p, int b, int L, int row, PageWin& pw) {
   int pi = uniform(row / PS - pw.base);
-  if (pi >= 128) {
+  if (pi >= WIN) {
     wait_vmcnt<0>();
-    load_page_window(p, b, ceil_div(L, PS), row / PS, pw);
+    load_page_window<WIN>(p, b, ceil_div(L, PS), row / PS, pw);
     pi = 0;
   }
+  if (WIN <= 64) return uniform(__builtin_amdgcn_readlane(pw.lo, pi));
   return uniform(pi < 64 ? __builtin_amdgcn_readlane(pw.lo, pi) : __builtin_amdgcn_readlane(pw.hi, pi - 64));
 }
+
+template <bool FP8>
+constexpr int page_window() { return FP8 ? 64 : 128; }
 
 // DMA instructions one wave issues for a full tile.
 template <bool FP8>
@@ -402,7 +415,7 @@ __device__ __forceinline__ TileLoad prepare_tile(const Params& p, uint8_t* smem,
       lds_zero16(smem, rope + lane * 16);
       return tl;
     }
-    const int page = page_id<PS>(p, b, L, row0, pw);
+    const int page = page_id<PS, page_window<FP8>()>(p, b, L, row0, pw);
     const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_BF16;
     const int nvalid = L - row0;
     if (nvalid >= 8) return TileLoad{pg, lds0 + lat, lds0 + rope};
@@ -426,7 +439,7 @@ __device__ __forceinline__ TileLoad prepare_tile(const Params& p, uint8_t* smem,
       if (lane < 32) lds_zero16(smem, rope + lane * 16);
       return tl;
     }
-    const int page = page_id<PS>(p, b, L, row0, pw);
+    const int page = page_id<PS, page_window<FP8>()>(p, b, L, row0, pw);
     const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * ROWB_FP8;
     const int nvalid = L - row0;
     if (nvalid >= 8) return TileLoad{pg, lds0 + lat, lds0 + rope};
@@ -709,18 +722,37 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   block_barrier();  // tile t0 is in LDS
   f32x16 s_next{};
   if (ACTIVE) s_next = qk(buf_of(t0), no_fill);
+  const TileLoad no_load{nullptr, 0u, 0u};
   for (int t = t0; t < t1; ++t) {
     const f32x16 s = s_next;
+    TileLoad tl = no_load;
     const bool fast = c_pos && st.ref_ready && (t + 1) * TILE <= min_vis;
     if (t + 1 < t1) {
       wait_tile(t + 1, 1);
       wait_lgkm0();
       block_barrier();  // tile t+1 is in LDS; every wave is done with tile t-1's buffer
-      if (t + 3 < t1) issue_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
+      // Tile t+3 goes to the buffer of tile t-1.  Even waves issue their share
+      // now, odd waves at the P exchange below: two bursts of loads queue in the
+      // CU's address unit instead of one burst from all four waves.
+      if (t + 3 < t1) {
+        tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
+        if ((w & 1) == 0 || !ACTIVE) {
+#pragma unroll
+          for (int k = 0; k < LOADS; ++k) issue_tile_part<FP8>(tl, k);
+          tl = no_load;
+        }
+      }
       if (ACTIVE) {
-        if (fast) {
+        if (fast && !FP8) {
           const float nm = -st.m_ref;
           s_next = qk(buf_of(t + 1), [&](int k) { fast_piece(s, nm, k); });
+        } else if (fast) {
+          // fp8: the A operands' widening already fills the VALU slots between
+          // the MFMAs, so the softmax goes first
+          const float nm = -st.m_ref;
+#pragma unroll
+          for (int k = 0; k < QK_STEPS; ++k) fast_piece(s, nm, k);
+          s_next = qk(buf_of(t + 1), no_fill);
         } else {
           masked_softmax(s, t);
           s_next = qk(buf_of(t + 1), no_fill);
@@ -748,6 +780,8 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     u32x4 vraw[GV];
 #pragma unroll
     for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
+#pragma unroll
+    for (int k = 0; k < LOADS; ++k) issue_tile_part<FP8>(tl, k);
     *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own) = pc0;
     *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own + 1024) =
         pc1;
@@ -810,7 +844,7 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   // page ids of the segment, then the first three tiles in flight before the
   // query loads
   PageWin pw;
-  load_page_window(p, b, ceil_div(L, PS), uniform((t0 * TILE) / PS), pw);
+  load_page_window<page_window<FP8>()>(p, b, ceil_div(L, PS), uniform((t0 * TILE) / PS), pw);
   issue_tile<FP8, PS>(p, smem, 0, b, L, t0, pw);
   if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1, pw);
   if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2, pw);

@@ -134,6 +134,21 @@ def test_segment_cost_split(cost, grid):
     print("segment cost", cost, "grid", grid, stats, flush=True)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("grid", [2, 0])
+def test_page_window_refill(kv_dtype, grid):
+    """Page size 16 with a few thousand rows: a segment crosses several 64- or
+    128-entry windows of block-table entries, so page ids are reloaded mid-loop."""
+    binding.set_grid_override(grid)
+    fp8 = kv_dtype != "bf16"
+    w = make_workload("refill", seed=31, batch=2, seq_len_range=(2500, 4200), num_heads=32, q_len=2, page_size=16,
+                      kv_dtype=kv_dtype, kv_value_scale=0.5 if fp8 else 1.0,
+                      bmm1_scale=INV_SQRT_192 * (0.02 if fp8 else 1.0), bmm2_scale=0.02 if fp8 else 1.0,
+                      causal=True, want_lse=True)
+    stats = compare_with_oracle(w)
+    print("refill", kv_dtype, grid, stats, flush=True)
+
+
 def test_deterministic_and_permutation_invariant():
     w = named_workload("tiny_bf16")
     o1, l1 = run_hip(w)
