@@ -95,7 +95,7 @@ def profiled_traffic(workload):
     return None
 
 
-def run_workload(name, steps, warmup, want_cpu):
+def run_workload(name, steps, warmup, want_cpu, rotate=3):
     import numpy as np
     import torch
     from paged_mla_decode_03_amd import binding
@@ -121,13 +121,20 @@ def run_workload(name, steps, warmup, want_cpu):
                    bmm2_scale=w.bmm2_scale, causal=w.causal)
     dims, max_q_len, _, _ = binding.dims_for(q, t["kv"], t["block_tables"], t["seq_lens"], t["qo_indptr"], max_q)
     stream = torch.cuda.current_stream().cuda_stream
-    args = (q.data_ptr(), t["kv"].data_ptr(), t["block_tables"].data_ptr(), t["seq_lens"].data_ptr(),
-            None if t["qo_indptr"] is None else t["qo_indptr"].data_ptr(), w.max_seq_len, max_q_len, w.bmm1_scale,
-            w.bmm2_scale, w.causal, out.data_ptr(), None if lse is None else lse.data_ptr(), ws.data_ptr(),
-            nbytes, dims, stream)
+    # Consecutive steps read different copies of the KV cache (and Q), so that a
+    # step never finds the previous step's data in L2 or the 256 MB MALL: a
+    # serving loop reads each layer's cache once per step.
+    kvs = [t["kv"]] + [t["kv"].clone() for _ in range(max(1, rotate) - 1)]
+    qs = [q] + [q.clone() for _ in range(max(1, rotate) - 1)]
+    arg_sets = [(qq.data_ptr(), kv.data_ptr(), t["block_tables"].data_ptr(), t["seq_lens"].data_ptr(),
+                 None if t["qo_indptr"] is None else t["qo_indptr"].data_ptr(), w.max_seq_len, max_q_len,
+                 w.bmm1_scale, w.bmm2_scale, w.causal, out.data_ptr(), None if lse is None else lse.data_ptr(),
+                 ws.data_ptr(), nbytes, dims, stream) for qq, kv in zip(qs, kvs)]
+    n_step = [0]
 
     def step():
-        rc = binding.mla_decode_paged(*args)
+        rc = binding.mla_decode_paged(*arg_sets[n_step[0] % len(arg_sets)])
+        n_step[0] += 1
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
@@ -179,7 +186,7 @@ def run_workload(name, steps, warmup, want_cpu):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if kv_bytes_per == 2 else dtype,
-        "data": "synthetic (seeded N(0,1) bf16 q/kv, shuffled pages)",
+        "data": f"synthetic (seeded N(0,1) q/kv, shuffled pages; {max(1, rotate)} cache copies rotated across steps)",
         "config": {"workload": name, "batch": B, "heads": H,
                    "q_len": spec.get("q_len") if "q_len_range" not in spec else list(spec["q_len_range"]),
                    "seq_lens": list(spec["seq_len_range"]) if "seq_len_range" in spec else
@@ -205,6 +212,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps first: the GPU reaches steady clocks only after tens of ms of work")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="copies of the KV cache and Q read in turn by consecutive steps (1 = one copy, which "
+                         "can sit in the 256 MB MALL for the smaller workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also time the other workloads (lines on stderr)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -219,13 +229,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    res = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
+    res = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, args.rotate)
     if args.all:
         from paged_mla_decode_03_amd.inputs import WORKLOAD_ORDER
         for name in WORKLOAD_ORDER:
             if name == args.workload:
                 continue
-            r = run_workload(name, args.steps, args.warmup, False)
+            r = run_workload(name, args.steps, args.warmup, False, args.rotate)
             log("[bench-extra] " + json.dumps(r))
     if args.copy_bytes > 0:
         n = (args.copy_bytes + 15) // 16 * 16
