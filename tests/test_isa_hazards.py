@@ -54,6 +54,44 @@ def test_library_kernels_have_no_mfma_hazards(library_asm, decode_bodies):
         assert sum("v_mfma" in l for l in body) >= 68, name  # 36 QK^T + 32 P.V steps per tile
 
 
+def _loop_depths(body):
+    """(depth, line) for each instruction line: the loop depth the compiler
+    annotates on the basic block that holds it (0 outside loops)."""
+    depth = 0
+    out = []
+    for line in body:
+        if re.match(r"\s*(\.LBB|; %bb)", line):
+            m = re.search(r"Depth=(\d+)", line)
+            depth = int(m.group(1)) if m else 0
+        out.append((depth, line))
+    return out
+
+
+def test_tile_loops_never_touch_scratch(decode_bodies):
+    """A scratch reload inside the tile loop comes with a full vmcnt wait, which
+    would drain the ring of tile loads in flight; register pressure in the tile
+    loop must stay below spilling."""
+    for name, body in decode_bodies.items():
+        lines = _loop_depths(body)
+        mfma_depth = max(d for d, l in lines if "v_mfma" in l)
+        assert mfma_depth >= 1, name
+        bad = [l.strip() for d, l in lines if d >= mfma_depth and "scratch_" in l]
+        assert not bad, (name, bad[:4])
+
+
+def test_scratch_check_sees_a_loop_reload():
+    body = [".LBB0_1:                                ; =>This Inner Loop Header: Depth=1",
+            "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]",
+            "\tscratch_load_dword v30, off, off ; 4-byte Folded Reload",
+            "\ts_cbranch_scc1 .LBB0_1",
+            "; %bb.2:",
+            "\tscratch_store_dword off, v30, off"]
+    lines = _loop_depths(body)
+    depth = max(d for d, l in lines if "v_mfma" in l)
+    assert depth == 1
+    assert [l for d, l in lines if d >= depth and "scratch_" in l] == [body[2]]
+
+
 PROBE = r'''
 #include <hip/hip_runtime.h>
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
