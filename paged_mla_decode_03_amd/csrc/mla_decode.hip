@@ -1051,10 +1051,24 @@ void mla_decode_kernel(Params p) {
 
 // ---------------------------------------------------------------- split merge
 
+// Max / sum over the 64 lanes of a wave, result in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 // One wave per (query row, head): combine the segments of its unit,
 // M = max_s m_s, w_s = 2^(m_s - M), out = bmm2 * sum w_s O_s / sum w_s l_s,
 // lse = ln2 * (M + log2 sum w_s l_s).  A unit done by one workgroup has a single
-// segment (w = 1): the same formula normalises it.
+// segment (w = 1): the same formula normalises it.  The loads of all segments'
+// (max, sum) and of eight segments' O are in flight together: the kernel is
+// bound by memory latency otherwise.  The summation order is fixed.
 __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6);
@@ -1084,23 +1098,46 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int U0 = p.ws_plan[2 + b] + pb * T + (u + 1) * p.seg_cost;  // cost position of the unit's first tile
   const int g0 = U0 / C;
   const int g1 = (U0 + T - 1) / C;
+  const int nseg = g1 - g0 + 1;
+  const float* mlb = p.ws_ml + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * 2;  // segment s at + s * PAIRS_BLOCK * 2
+  const uint16_t* ob = p.ws_o + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * D_V + 8 * lane;
+  // (max, sum) of up to 64 segments at a time, one per lane, all loads in flight together
   float M = -INFINITY;
-  for (int g = g0; g <= g1; ++g) M = fmaxf(M, p.ws_ml[((size_t)(g + u) * PAIRS_BLOCK + pl) * 2]);
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int c0 = 0; c0 < nseg; c0 += 64) {
+    if (c0 + lane < nseg) M = fmaxf(M, mlb[(size_t)(c0 + lane) * PAIRS_BLOCK * 2]);
+  }
+  M = wave_max(M);
   float den = 0.f;
-  for (int g = g0; g <= g1; ++g) {
-    const size_t slot = (size_t)(g + u);
-    const float* ml = p.ws_ml + (slot * PAIRS_BLOCK + pl) * 2;
-    const float m = ml[0];
-    const float wgt = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-    den += wgt * ml[1];
-    const u32x4 o = *(const u32x4*)(p.ws_o + (slot * PAIRS_BLOCK + pl) * D_V + 8 * lane);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int c0 = 0; c0 < nseg; c0 += 64) {
+    float wl = 0.f;  // this lane's segment weight 2^(m - M)
+    if (c0 + lane < nseg) {
+      const float* ml = mlb + (size_t)(c0 + lane) * PAIRS_BLOCK * 2;
+      const float m = ml[0];
+      wl = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      den += wl * ml[1];
+    }
+    // O of eight segments in flight at a time; lane holds dims 8 lane .. 8 lane + 8
+    const int cn = min(64, nseg - c0);
+    for (int s0 = 0; s0 < cn; s0 += 8) {
+      u32x4 o[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += wgt * __uint_as_float(o[e] << 16);
-      acc[2 * e + 1] += wgt * __uint_as_float(o[e] & 0xffff0000u);
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < cn) o[i] = *(const u32x4*)(ob + (size_t)(c0 + s0 + i) * PAIRS_BLOCK * D_V);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (s0 + i < cn) {
+          const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s0 + i));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += w * __uint_as_float(o[i][e] << 16);
+            acc[2 * e + 1] += w * __uint_as_float(o[i][e] & 0xffff0000u);
+          }
+        }
+      }
     }
   }
+  den = wave_sum(den);
   const float inv = p.bmm2 / den;
   u32x4 packed;
 #pragma unroll
