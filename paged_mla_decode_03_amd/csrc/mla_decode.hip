@@ -389,9 +389,10 @@ constexpr int tile_loads() { return FP8 ? 5 : 9; }
 // prepare_tile() does everything except the DMA of a full 8-row share: rows at
 // or past seq_len are never read from memory (nor is their block-table entry)
 // and are zero-filled; a share cut by seq_len is loaded at once.  A full share
-// is returned for issue_tile_part(), one DMA instruction per call, so that the
-// instructions can be spread between MFMAs: a burst of them stalls the wave's
-// instruction stream while the CU's address unit works through them.
+// is returned for issue_tile_share(), so that the caller picks the moment: a
+// burst of DMA instructions stalls the issuing wave while the CU's address
+// unit works through them, and bursts from several waves queue behind each
+// other.
 struct TileLoad {
   const uint8_t* pg;  // global address of the share's first row; null: nothing left to issue
   uint32_t lat;       // LDS byte address of the share's first latent row
@@ -462,39 +463,63 @@ __device__ __forceinline__ TileLoad prepare_tile(const Params& p, uint8_t* smem,
   return tl;
 }
 
-// DMA instruction k (0 .. tile_loads<FP8>() - 1) of a full share.
+// Four DMA instructions with one m0: the instruction offsets 0, 1024, 2048 and
+// 3072 step the LDS destination m0 + offset + 16 * lane and the global address
+// sbase + voff + offset together, so rows whose global stride differs from
+// their 1 KiB LDS stride carry the difference in their lane offsets.  Writing
+// m0 costs the issuing wave about ten cycles per LDS-DMA instruction that
+// follows it, so it is written once per four instructions.
+__device__ __forceinline__ void dma16x4_s(const void* sbase, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                          uint32_t lds_wave_base) {
+  const uint64_t sb = (uint64_t)(uintptr_t)sbase;
+  const uint64_t sbu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  asm volatile(
+      "s_mov_b32 m0, %5\n\t"
+      "global_load_lds_dwordx4 %0, %4\n\t"
+      "global_load_lds_dwordx4 %1, %4 offset:1024\n\t"
+      "global_load_lds_dwordx4 %2, %4 offset:2048\n\t"
+      "global_load_lds_dwordx4 %3, %4 offset:3072"
+      :
+      : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"((const void*)(uintptr_t)sbu), "s"(m0)
+      : "memory");
+}
+
+// The DMA instructions of a full share (tile_loads<FP8>() of them, in a fixed
+// order); nothing for an empty share.
 template <bool FP8>
-__device__ __forceinline__ void issue_tile_part(const TileLoad& tl, int k) {
+__device__ __forceinline__ void issue_tile_share(const TileLoad& tl) {
   if (tl.pg == nullptr) return;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   if (!FP8) {
-    if (k < 8) {
-      dma16_s(tl.pg + k * ROWB_BF16, (uint32_t)((lane ^ swz_lat_bf16(8 * w + k)) << 4), tl.lat + k * 1024);
-    } else {
-      const int rr = lane >> 3;
-      dma16_s(tl.pg, (uint32_t)(rr * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_rope_bf16(8 * w + rr)) << 4)), tl.rope);
-    }
+    // latent row i: global pg + 1152 i + 16 (lane ^ swz), LDS lat + 1024 i + 16 lane
+    auto voff = [&](int i) { return (uint32_t)(((lane ^ swz_lat_bf16(8 * w + i)) << 4) + 128 * (i & 3)); };
+    dma16x4_s(tl.pg, voff(0), voff(1), voff(2), voff(3), tl.lat);
+    dma16x4_s(tl.pg + 4 * ROWB_BF16, voff(4), voff(5), voff(6), voff(7), tl.lat + 4096);
+    const int rr = lane >> 3;
+    dma16_s(tl.pg, (uint32_t)(rr * ROWB_BF16 + 1024 + (((lane & 7) ^ swz_rope_bf16(8 * w + rr)) << 4)), tl.rope);
   } else {
+    // latent rows 2k, 2k+1 (lane halves): global pg + 1152 k + 576 hi, LDS lat + 1024 k
     const int hi = lane >> 5;
-    if (k < 4) {
-      dma16_s(tl.pg + 2 * k * ROWB_FP8,
-              (uint32_t)(hi * ROWB_FP8 + (((lane & 31) ^ swz_lat_fp8(8 * w + 2 * k + hi)) << 4)), tl.lat + k * 1024);
-    } else if (lane < 32) {
+    auto voff = [&](int k) {
+      return (uint32_t)(hi * ROWB_FP8 + (((lane & 31) ^ swz_lat_fp8(8 * w + 2 * k + hi)) << 4) + 128 * k);
+    };
+    dma16x4_s(tl.pg, voff(0), voff(1), voff(2), voff(3), tl.lat);
+    if (lane < 32) {
       const int rr = lane >> 2;
       dma16_s(tl.pg, (uint32_t)(rr * ROWB_FP8 + 512 + (((lane & 3) ^ swz_rope_fp8(8 * w + rr)) << 4)), tl.rope);
     }
   }
 }
 
-// A whole tile load at once (prologue, and waves without MFMA work).
-// A full tile costs each wave exactly tile_loads<FP8>() DMA instructions.
+// A whole tile load at once.  A full tile costs each wave exactly
+// tile_loads<FP8>() DMA instructions.
 template <bool FP8, int PS>
 __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t,
                                            PageWin& pw) {
-  const TileLoad tl = prepare_tile<FP8, PS>(p, smem, buf, b, L, t, pw);
-#pragma unroll
-  for (int k = 0; k < tile_loads<FP8>(); ++k) issue_tile_part<FP8>(tl, k);
+  issue_tile_share<FP8>(prepare_tile<FP8, PS>(p, smem, buf, b, L, t, pw));
 }
 
 // ---------------------------------------------------------------- one segment
@@ -737,8 +762,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       if (t + 3 < t1) {
         tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
         if ((w & 1) == 0 || !ACTIVE) {
-#pragma unroll
-          for (int k = 0; k < LOADS; ++k) issue_tile_part<FP8>(tl, k);
+          issue_tile_share<FP8>(tl);
           tl = no_load;
         }
       }
@@ -780,8 +804,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     u32x4 vraw[GV];
 #pragma unroll
     for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
-#pragma unroll
-    for (int k = 0; k < LOADS; ++k) issue_tile_part<FP8>(tl, k);
+    issue_tile_share<FP8>(tl);
     *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own) = pc0;
     *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own + 1024) =
         pc1;
