@@ -55,6 +55,9 @@ class MlaProblem:
     block_tables  int32 [B, W]
     seq_lens      int32 [B]
     qo_indptr     int32 [B+1] or None (then every request has q_len_fixed rows)
+    sinks         float [H] or None: per-head sink logits (natural-log units, on
+                  the scale of bmm1_scale * q.k), one more term of every softmax
+                  denominator with no value row
     """
 
     q_bits: np.ndarray
@@ -67,6 +70,7 @@ class MlaProblem:
     bmm1_scale: float
     bmm2_scale: float
     causal: bool
+    sinks: Optional[np.ndarray] = None
 
     @property
     def batch(self):
@@ -148,6 +152,11 @@ def _masked_logits(problem, b, Kb, lo=0, hi=None):
 def reference_decode(problem, requests=None):
     """Full decode.  Returns (out float64 [R, H, 512], lse float64 [R, H]).
 
+    With sinks, each (row, head) softmax has one more term exp(sink_h) in its
+    denominator and none in the numerator; lse is then ln of that whole
+    denominator (FlashInfer issue #3131, launcher excerpt: attention_sinks;
+    the pages give no formula, this is the plain reading).
+
     Rows of requests not listed in `requests` are left NaN (lets tests sample
     a few requests of a large launch).
     """
@@ -161,8 +170,14 @@ def reference_decode(problem, requests=None):
         Kb = gather_request_rows(problem, b)
         S, _ = _masked_logits(problem, b, Kb)
         m = S.max(axis=1, keepdims=True)
+        if problem.sinks is not None:
+            # the sink is one more logit of the softmax, attached to a zero value row
+            sink = np.tile(np.asarray(problem.sinks, dtype=np.float64), q_b)[:, None]  # row index = i*H + h
+            m = np.maximum(m, sink)
         e = np.exp(S - m)
         Z = e.sum(axis=1, keepdims=True)
+        if problem.sinks is not None:
+            Z = Z + np.exp(sink - m)
         P = e / Z
         O = (P @ Kb[:, :D_LATENT]) * float(problem.bmm2_scale)
         out[r_b:r_b + q_b] = O.reshape(q_b, H, D_LATENT)

@@ -128,6 +128,73 @@ def test_scale_linearity_and_zero_bmm1():
             np.testing.assert_allclose(l0[2 * b + i], math.log(n), **TIGHT)
 
 
+# ---------------------------------------------------------------- attention sinks
+
+def _with_sinks(prob, sinks):
+    import dataclasses
+    return dataclasses.replace(prob, sinks=np.asarray(sinks, dtype=np.float64))
+
+
+def test_sink_seq_len_one_is_a_logistic_gate():
+    """L = 1 with a sink: the one real key competes with the sink alone, so
+    out = bmm2 * V[0] * e^s / (e^s + e^sink) and lse = ln(e^s + e^sink)."""
+    rng = np.random.default_rng(21)
+    H = 16
+    q, ks = random_dense(rng, 2, H, [1, 1], [1, 1])
+    prob = build_paged(q, ks, 32, rng=rng, bmm1=0.3, bmm2=1.5)
+    sinks = rng.normal(0.0, 2.0, size=H)
+    sinks[0], sinks[1] = 40.0, -40.0  # a dominating sink and a negligible one
+    out, lse = oracle.reference_decode(_with_sinks(prob, sinks))
+    for b in range(2):
+        for h in range(H):
+            s = 0.3 * float(q[b, h] @ ks[b][0])
+            gate = 1.0 / (1.0 + math.exp(sinks[h] - s))
+            np.testing.assert_allclose(out[b, h], 1.5 * gate * ks[b][0, :512], rtol=1e-12, atol=1e-300)
+            assert abs(lse[b, h] - np.logaddexp(s, sinks[h])) < 1e-12
+
+
+def test_sink_with_equal_logits():
+    """Equal logits s over n visible rows plus a sink: out = bmm2 * mean(V) *
+    n e^s / (n e^s + e^sink), lse = ln(n e^s + e^sink)."""
+    rng = np.random.default_rng(22)
+    H = 16
+    q_lens, L = [3], [70]
+    q, ks = random_dense(rng, 1, H, q_lens, L)
+    q[..., :512] = 0.0
+    rope = bf16_round(rng.standard_normal(64).astype(np.float32))
+    ks[0][:, 512:] = rope
+    prob = build_paged(q, ks, 32, rng=rng, q_lens=q_lens, bmm1=0.21, bmm2=0.5, causal=True)
+    sinks = rng.normal(1.0, 3.0, size=H)
+    out, lse = oracle.reference_decode(_with_sinks(prob, sinks))
+    for i in range(3):
+        n = 70 - 3 + i + 1
+        mean_v = ks[0][:n, :512].mean(axis=0)
+        for h in range(H):
+            s = 0.21 * float(q[i, h, 512:] @ rope)
+            frac = n * math.exp(s) / (n * math.exp(s) + math.exp(sinks[h]))
+            np.testing.assert_allclose(out[i, h], 0.5 * frac * mean_v, rtol=1e-12, atol=1e-14)
+            assert abs(lse[i, h] - np.logaddexp(s + math.log(n), sinks[h])) < 1e-12
+
+
+def test_sink_is_a_zero_value_partial():
+    """Merging the sink-free decode's (O, lse) with one more partial (O = 0,
+    lse = sink) reproduces the decode with the sink; a sink at -inf changes
+    nothing, bit for bit."""
+    rng = np.random.default_rng(23)
+    H = 32
+    q, ks = random_dense(rng, 2, H, [2, 2], [90, 41])
+    prob = build_paged(q, ks, 32, rng=rng, bmm1=0.09, bmm2=1.25, causal=True)
+    sinks = rng.normal(0.0, 2.0, size=H)
+    o0, l0 = oracle.reference_decode(prob)
+    o1, l1 = oracle.reference_decode(_with_sinks(prob, sinks))
+    sink_rows = np.tile(sinks, (4, 1))
+    mo, ml = oracle.merge_partials([(o0 / 1.25, l0), (np.zeros_like(o0), sink_rows)], 1.25)
+    np.testing.assert_allclose(mo, o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ml, l1, rtol=1e-12, atol=1e-13)
+    o2, l2 = oracle.reference_decode(_with_sinks(prob, np.full(H, -np.inf)))
+    assert np.array_equal(o2, o0) and np.array_equal(l2, l0)
+
+
 # ---------------------------------------------------------------- brute force / library
 
 @pytest.mark.parametrize("causal", [True, False])
