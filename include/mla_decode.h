@@ -40,7 +40,7 @@ enum {
   MLA_ERR_BAD_PAGE_SIZE = 3,     /* page_size not in {16, 32, 64} */
   MLA_ERR_BAD_HEAD_DIMS = 4,     /* kv_lora_rank != 512 or qk_rope_head_dim != 64 */
   MLA_ERR_BAD_DTYPE = 5,         /* kv_dtype not MLA_KV_BF16 / MLA_KV_FP8_E4M3FN */
-  MLA_ERR_MISALIGNED = 6,        /* q, kv_cache, out or workspace not 16-byte aligned */
+  MLA_ERR_MISALIGNED = 6,        /* q, kv_cache, out or workspace not 16-byte aligned; lse or an option pointer not 4-byte aligned */
   MLA_ERR_WORKSPACE_TOO_SMALL = 7,
   MLA_ERR_BAD_Q_LEN = 8,         /* max_q_len < 1, fixed launch with q_len_fixed != max_q_len,
                                     or total_q inconsistent with a fixed launch */
@@ -112,6 +112,41 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
                      int32_t max_q_len, float bmm1_scale, float bmm2_scale, int causal, void* out,
                      float* lse, void* workspace, size_t workspace_bytes,
                      const mla_decode_dims_t* dims, void* stream);
+
+/*
+ * Device-resident options of mla_decode_paged_ex.  Each pointer may be NULL.
+ *
+ * bmm1_scale  device float32 scalar.  When set it replaces the bmm1_scale
+ *             argument, read by the kernels at run time (FlashInfer PR #1248,
+ *             "dynamic scale factor interface"; issue #3131, Python API:
+ *             bmm1_scale / bmm2_scale may be a tensor), so a captured HIP
+ *             graph follows scale updates made between its replays.
+ * bmm2_scale  device float32 scalar, likewise for bmm2_scale.
+ * sinks       device float32 [num_heads]: per-head attention-sink logits, in
+ *             natural-log units on the scale of bmm1_scale * q.k (issue #3131,
+ *             launcher excerpt: attention_sinks).  Each (row, head) softmax
+ *             gains one term exp(sinks[h]) in its denominator and none in its
+ *             numerator; lse, when requested, is ln of that whole denominator.
+ * All three must be 4-byte aligned and stay valid until the enqueued work
+ * completes; the library only reads them.
+ */
+typedef struct {
+  const float* bmm1_scale;
+  const float* bmm2_scale;
+  const float* sinks;
+} mla_decode_options_t;
+
+/*
+ * mla_decode_paged_ex -- mla_decode_paged with device-resident options.
+ * Arguments as mla_decode_paged; opts may be NULL (then identical to it).
+ * Same workspace, same errors, plus MLA_ERR_MISALIGNED for an option pointer
+ * that is not 4-byte aligned.
+ */
+int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* block_tables,
+                        const int32_t* seq_lens, const int32_t* qo_indptr, int32_t max_seq_len,
+                        int32_t max_q_len, float bmm1_scale, float bmm2_scale, int causal, void* out,
+                        float* lse, void* workspace, size_t workspace_bytes,
+                        const mla_decode_dims_t* dims, void* stream, const mla_decode_options_t* opts);
 
 /*
  * Bytes of workspace mla_decode_paged needs for this shape on the current

@@ -28,6 +28,14 @@ QK_ROPE_HEAD_DIM = 64
 D_QK = KV_LORA_RANK + QK_ROPE_HEAD_DIM
 
 
+class MlaOptions(ctypes.Structure):
+    _fields_ = [
+        ("bmm1_scale", ctypes.c_void_p),
+        ("bmm2_scale", ctypes.c_void_p),
+        ("sinks", ctypes.c_void_p),
+    ]
+
+
 class MlaDims(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -58,6 +66,9 @@ def load_library():
     lib.mla_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, sz,
                                      ctypes.POINTER(MlaDims), vp]
     lib.mla_decode_paged.restype = ctypes.c_int
+    lib.mla_decode_paged_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, sz,
+                                        ctypes.POINTER(MlaDims), vp, ctypes.POINTER(MlaOptions)]
+    lib.mla_decode_paged_ex.restype = ctypes.c_int
     lib.mla_decode_paged_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int]
     lib.mla_decode_paged_workspace_size.restype = sz
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -106,6 +117,19 @@ def mla_decode_paged(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len
         _ptr(q), _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(qo_indptr), int(max_seq_len),
         int(max_q_len), float(bmm1_scale), float(bmm2_scale), int(bool(causal)), _ptr(out), _ptr(lse),
         _ptr(workspace), int(workspace_bytes), ctypes.byref(dims), stream))
+
+
+def mla_decode_paged_ex(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q_len, bmm1_scale,
+                        bmm2_scale, causal, out, lse, workspace, workspace_bytes, dims, opts, stream=None):
+    """Direct call of the C entry point with device-resident options (an
+    MlaOptions or None).  Returns the status."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().mla_decode_paged_ex(
+        _ptr(q), _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(qo_indptr), int(max_seq_len),
+        int(max_q_len), float(bmm1_scale), float(bmm2_scale), int(bool(causal)), _ptr(out), _ptr(lse),
+        _ptr(workspace), int(workspace_bytes), ctypes.byref(dims), stream,
+        None if opts is None else ctypes.byref(opts)))
 
 
 def set_grid_override(grid):
@@ -186,10 +210,22 @@ def workspace_bytes_for(query, kv_cache, block_tables, seq_lens, max_seq_len, *,
     return n
 
 
+def _device_scalar(name, v, device):
+    if not isinstance(v, torch.Tensor):
+        return None
+    if v.dtype != torch.float32 or v.numel() != 1 or not v.is_cuda or v.device != device:
+        raise TypeError(f"{name} as a tensor must be one float32 element on the query's device")
+    return v
+
+
 def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_len, *, qo_indptr=None,
            max_seq_len_q=None, out=None, lse=None, return_lse=False, bmm1_scale=1.0, bmm2_scale=1.0,
-           causal=True):
-    """Batched paged MLA decode.  Returns out, or (out, lse) with return_lse."""
+           causal=True, sinks=None):
+    """Batched paged MLA decode.  Returns out, or (out, lse) with return_lse.
+
+    bmm1_scale / bmm2_scale: a float, or a one-element float32 device tensor
+    read by the kernels at run time (so a captured graph follows updates).
+    sinks: None or a float32 device tensor [H] of per-head sink logits."""
     for name, t in (("query", query), ("kv_cache", kv_cache), ("workspace_buffer", workspace_buffer),
                     ("block_tables", block_tables), ("seq_lens", seq_lens)):
         if not t.is_cuda:
@@ -217,8 +253,19 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
     else:
         lse = None
     ws_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
-    rc = mla_decode_paged(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q, bmm1_scale,
-                          bmm2_scale, causal, out, lse, workspace_buffer, ws_bytes, dims)
+    b1 = _device_scalar("bmm1_scale", bmm1_scale, query.device)
+    b2 = _device_scalar("bmm2_scale", bmm2_scale, query.device)
+    if sinks is not None and (sinks.dtype != torch.float32 or tuple(sinks.shape) != (H,) or not sinks.is_cuda
+                              or not sinks.is_contiguous()):
+        raise TypeError(f"sinks must be a contiguous float32 device tensor of shape ({H},)")
+    if b1 is None and b2 is None and sinks is None:
+        rc = mla_decode_paged(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q, bmm1_scale,
+                              bmm2_scale, causal, out, lse, workspace_buffer, ws_bytes, dims)
+    else:
+        opts = MlaOptions(_ptr(b1), _ptr(b2), _ptr(sinks))
+        rc = mla_decode_paged_ex(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q,
+                                 1.0 if b1 is not None else bmm1_scale, 1.0 if b2 is not None else bmm2_scale,
+                                 causal, out, lse, workspace_buffer, ws_bytes, dims, opts)
     if rc != MLA_OK:
         raise RuntimeError(f"mla_decode_paged failed: {mla_status_string(rc)} (status {rc})")
     return (out, lse) if return_lse else out

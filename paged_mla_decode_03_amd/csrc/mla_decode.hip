@@ -115,6 +115,9 @@ struct Params {
   float bmm2;
   int32_t causal;
   int32_t seg_cost;  // cost of starting a segment, in tiles (see the work plan)
+  const float* bmm1_dev;  // device bmm1_scale (replaces scale_log2 / LOG2E) or null
+  const float* bmm2_dev;  // device bmm2_scale (replaces bmm2) or null
+  const float* sinks;     // device [heads] sink logits (natural log) or null
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -987,6 +990,7 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
 template <bool FP8, int PS>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(Params p) {
+  if (p.bmm1_dev != nullptr) p.scale_log2 = *p.bmm1_dev * LOG2E;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   // The plan lives in LDS only until this workgroup has found its starting point.
   int* tile_off = (int*)(smem + PLAN_SCRATCH_OFF);
@@ -1130,6 +1134,10 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
     if (c0 + lane < nseg) M = fmaxf(M, mlb[(size_t)(c0 + lane) * PAIRS_BLOCK * 2]);
   }
   M = wave_max(M);
+  // a sink is one more softmax term with no value row: it joins the max and
+  // the denominator
+  const float sink = (p.sinks != nullptr) ? p.sinks[head] * LOG2E : -INFINITY;
+  M = fmaxf(M, sink);
   float den = 0.f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int c0 = 0; c0 < nseg; c0 += 64) {
@@ -1161,7 +1169,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
     }
   }
   den = wave_sum(den);
-  const float inv = p.bmm2 / den;
+  if (sink != -INFINITY) den += __builtin_amdgcn_exp2f(sink - M);
+  const float inv = ((p.bmm2_dev != nullptr) ? *p.bmm2_dev : p.bmm2) / den;
   u32x4 packed;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -1261,7 +1270,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_BAD_PAGE_SIZE: return "page_size must be 16, 32 or 64";
     case MLA_ERR_BAD_HEAD_DIMS: return "kv_lora_rank must be 512 and qk_rope_head_dim 64";
     case MLA_ERR_BAD_DTYPE: return "kv_dtype must be bf16 or fp8 e4m3fn";
-    case MLA_ERR_MISALIGNED: return "q, kv_cache, out and workspace must be 16-byte aligned";
+    case MLA_ERR_MISALIGNED: return "misaligned pointer (q, kv_cache, out, workspace: 16 bytes; lse, options: 4)";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than mla_decode_paged_workspace_size()";
     case MLA_ERR_BAD_Q_LEN: return "inconsistent query lengths (max_q_len, q_len_fixed, total_q)";
     case MLA_ERR_BAD_BLOCK_TABLE: return "block_table_stride * page_size < max_seq_len";
@@ -1286,7 +1295,18 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
                      const int32_t* qo_indptr, int32_t max_seq_len, int32_t max_q_len, float bmm1_scale,
                      float bmm2_scale, int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
                      const mla_decode_dims_t* dims, void* stream) {
+  return mla_decode_paged_ex(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q_len, bmm1_scale,
+                             bmm2_scale, causal, out, lse, workspace, workspace_bytes, dims, stream, nullptr);
+}
+
+int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* qo_indptr, int32_t max_seq_len, int32_t max_q_len, float bmm1_scale,
+                        float bmm2_scale, int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        const mla_decode_dims_t* dims, void* stream, const mla_decode_options_t* opts) {
   if (!q || !kv_cache || !block_tables || !seq_lens || !out || !workspace || !dims) return MLA_ERR_NULL_POINTER;
+  if (opts != nullptr &&
+      (((uintptr_t)opts->bmm1_scale | (uintptr_t)opts->bmm2_scale | (uintptr_t)opts->sinks) & 3))
+    return MLA_ERR_MISALIGNED;
   const int v = validate(dims, max_seq_len, max_q_len, qo_indptr != nullptr);
   if (v != MLA_OK) return v;
   if (((uintptr_t)q | (uintptr_t)kv_cache | (uintptr_t)out | (uintptr_t)workspace) & 15) return MLA_ERR_MISALIGNED;
@@ -1319,6 +1339,9 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
   p.bmm2 = bmm2_scale;
   p.causal = causal ? 1 : 0;
   p.seg_cost = g_seg_cost.load(std::memory_order_relaxed);
+  p.bmm1_dev = opts ? opts->bmm1_scale : nullptr;
+  p.bmm2_dev = opts ? opts->bmm2_scale : nullptr;
+  p.sinks = opts ? opts->sinks : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = dims->kv_dtype == MLA_KV_FP8_E4M3FN;

@@ -84,3 +84,23 @@ def test_bad_arguments(dims_over, call_over, code):
 
 def test_workspace_size_zero_for_rejected_shape():
     assert binding.mla_decode_paged_workspace_size(_dims(num_heads=24), 128, 1) == 0
+
+
+MISALIGNED = 6
+
+
+def test_options_struct_and_misaligned_option_pointers():
+    # three pointers, in header order
+    assert ctypes.sizeof(binding.MlaOptions) == 24
+    assert binding.MlaOptions.sinks.offset == 16
+    for field in ("bmm1_scale", "bmm2_scale", "sinks"):
+        opts = binding.MlaOptions(None, None, None)
+        setattr(opts, field, FAKE + 2)
+        rc = binding.mla_decode_paged_ex(FAKE, FAKE, FAKE, FAKE, None, 128, 1, 1.0, 1.0, True, FAKE, None, FAKE,
+                                         1 << 30, _dims(), opts, stream=0)
+        assert rc == MISALIGNED, (field, rc)
+    # NULL options behave exactly like mla_decode_paged (here: the same shape error)
+    bad = _dims(num_heads=20)
+    rc_ex = binding.mla_decode_paged_ex(FAKE, FAKE, FAKE, FAKE, None, 128, 1, 1.0, 1.0, True, FAKE, None, FAKE,
+                                        1 << 30, bad, None, stream=0)
+    assert rc_ex == _call(bad)
