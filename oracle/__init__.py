@@ -32,6 +32,7 @@ from .mla import (
     gather_request_rows,
     reference_decode,
     reference_partial,
+    reference_dcp_partial,
     merge_partials,
 )
 
@@ -44,5 +45,6 @@ __all__ = [
     "gather_request_rows",
     "reference_decode",
     "reference_partial",
+    "reference_dcp_partial",
     "merge_partials",
 ]

@@ -221,3 +221,39 @@ def merge_partials(parts, bmm2_scale):
     W = w.sum(axis=0)
     out = float(bmm2_scale) * (w[..., None] * Os).sum(axis=0) / W[..., None]
     return out, M + np.log(W)
+
+
+def reference_dcp_partial(problem, rank, world):
+    """Sequence-sharded partial of every request: the share of rank `rank` of
+    `world` ranks, which hold the cached rows round-robin (global position t on
+    rank t mod world, in order).  Causal limits come from the global positions:
+    query row i of request b sees global positions t < L - q_b + i + 1.
+
+    Returns (out float64 [R, H, 512], lse float64 [R, H]) over the rank's rows:
+    out = bmm2 * softmax-normalised P.V and lse = ln sum exp(s) over the
+    visible rows the rank holds; a row that sees none of them gets out = 0 and
+    lse = -inf.  Merging every rank's partial with merge_partials (bmm2 = 1,
+    since each partial already carries it) gives the full decode (vLLM docs,
+    "FlashInferMLAImpl", forward_mqa: DCP passes cp_world, cp_rank and the
+    global causal lengths and consumes the natural-log LSE).
+    """
+    H = problem.num_heads
+    R = problem.q_bits.shape[0]
+    out = np.zeros((R, H, D_LATENT))
+    lse = np.full((R, H), -np.inf)
+    for b in range(problem.batch):
+        r_b, q_b, L = _check_request(problem, b)
+        Kb = gather_request_rows(problem, b)
+        S, visible = _masked_logits(problem, b, Kb)
+        mine = (np.arange(L) % world) == rank
+        visible = visible & mine[None, :]
+        any_vis = visible.any(axis=1)
+        S = np.where(visible, S, -np.inf)
+        m = np.where(any_vis, S.max(axis=1), 0.0)
+        e = np.where(visible, np.exp(S - m[:, None]), 0.0)
+        Z = e.sum(axis=1)
+        Zs = np.where(any_vis, Z, 1.0)
+        O = (e / Zs[:, None]) @ Kb[:, :D_LATENT] * float(problem.bmm2_scale)
+        out[r_b:r_b + q_b] = O.reshape(q_b, H, D_LATENT)
+        lse[r_b:r_b + q_b] = np.where(any_vis, m + np.log(Zs), -np.inf).reshape(q_b, H)
+    return out, lse

@@ -268,6 +268,38 @@ def test_split_merge_reproduces_full():
             np.testing.assert_allclose(ml, full_l[:ql], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("world", [2, 3, 8])
+def test_dcp_partials_merge_to_the_full_decode(world):
+    """Round-robin sequence shards: each rank's partial over its own rows,
+    merged by LSE weight, reproduces the unsharded decode; ranks that hold
+    no visible row of some query row report lse = -inf and out = 0."""
+    rng = np.random.default_rng(24)
+    H = 16
+    for causal, q_lens, L in [(True, [4, 1], [5, 123]), (False, [2, 3], [7, 64]), (True, [3, 3], [3, 40])]:
+        q, ks = random_dense(rng, 2, H, q_lens, L)
+        prob = build_paged(q, ks, 32, rng=rng, q_lens=q_lens, packed=True, bmm1=0.11, bmm2=1.3, causal=causal)
+        full_o, full_l = oracle.reference_decode(prob)
+        parts = [oracle.reference_dcp_partial(prob, r, world) for r in range(world)]
+        mo, ml = oracle.merge_partials(parts, 1.0)
+        np.testing.assert_allclose(mo, full_o, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(ml, full_l, rtol=1e-12, atol=1e-13)
+        # a rank with no visible row: the first request's first row sees L - q + 1 global rows
+        n0 = L[0] - q_lens[0] + 1 if causal else L[0]
+        for r in range(world):
+            if r >= n0:
+                assert np.all(parts[r][1][0] == -np.inf) and np.all(parts[r][0][0] == 0.0)
+
+
+def test_dcp_single_rank_is_the_full_decode():
+    rng = np.random.default_rng(25)
+    q, ks = random_dense(rng, 2, 16, [2, 2], [33, 80])
+    prob = build_paged(q, ks, 32, rng=rng, bmm1=0.2, bmm2=0.7, causal=True)
+    o, l = oracle.reference_decode(prob)
+    o1, l1 = oracle.reference_dcp_partial(prob, 0, 1)
+    np.testing.assert_allclose(o1, o, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l1, l, rtol=1e-13, atol=1e-15)
+
+
 def test_dense_rows_equal_single_row_decodes():
     """A dense multi-row request equals each of its rows run as its own q=1 request
     over the same cache (the flattening vLLM uses for non-causal blocks)."""
