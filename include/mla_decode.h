@@ -80,7 +80,8 @@ typedef struct mla_decode_dims {
  *              anything, NaN included, and never affect the result.
  * block_tables device, int32 [B, block_table_stride] row-major.  Only entries
  *              0 .. ceil(seq_lens[b]/page_size)-1 of row b are read.
- * seq_lens     device, int32 [B]; each in [1, max_seq_len].
+ * seq_lens     device, int32 [B]; each in [1, max_seq_len] (0 allowed in the
+ *              sequence-sharded mode of mla_decode_paged_ex).
  * qo_indptr    device, int32 [B+1] cumulative query offsets (starts at 0, strictly
  *              increasing, ends at total_q, deltas <= max_q_len), or NULL for a
  *              fixed launch where every request has q_len_fixed rows.
@@ -127,26 +128,65 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
  *             launcher excerpt: attention_sinks).  Each (row, head) softmax
  *             gains one term exp(sinks[h]) in its denominator and none in its
  *             numerator; lse, when requested, is ln of that whole denominator.
- * All three must be 4-byte aligned and stay valid until the enqueued work
+ * seq_lens_global
+ *             device int32 [B], or NULL: sequence-sharded (DCP) partial mode
+ *             (vLLM docs, "FlashInferMLAImpl", forward_mqa: cp_world, cp_rank,
+ *             causal_seqlens_kv_global).  The cache given to this call holds
+ *             rank cp_rank's share of each request: global positions
+ *             t = cp_rank (mod cp_world), in order, so local row j is global
+ *             position j * cp_world + cp_rank and seq_lens[b] counts the local
+ *             rows (0 allowed).  Causal limits come from the global lengths:
+ *             query row i sees global positions below
+ *             seq_lens_global[b] - q_b + i + 1.  out and lse are then this
+ *             rank's partial: bmm2 * the softmax-normalised P.V over the visible
+ *             local rows and ln of their exponent sum; a (row, head) with no
+ *             visible local row gets out = 0 and lse = -inf.  mla_merge_partials
+ *             combines the ranks' partials (lse is required in this mode).
+ * cp_world, cp_rank
+ *             1 <= cp_world, 0 <= cp_rank < cp_world; read only in DCP mode.
+ * All pointers must be 4-byte aligned and stay valid until the enqueued work
  * completes; the library only reads them.
  */
 typedef struct {
   const float* bmm1_scale;
   const float* bmm2_scale;
   const float* sinks;
+  const int32_t* seq_lens_global;
+  int32_t cp_world;
+  int32_t cp_rank;
 } mla_decode_options_t;
 
 /*
  * mla_decode_paged_ex -- mla_decode_paged with device-resident options.
  * Arguments as mla_decode_paged; opts may be NULL (then identical to it).
  * Same workspace, same errors, plus MLA_ERR_MISALIGNED for an option pointer
- * that is not 4-byte aligned.
+ * that is not 4-byte aligned, MLA_ERR_BAD_SHAPE for cp_world < 1 or cp_rank
+ * outside [0, cp_world), and MLA_ERR_NULL_POINTER for DCP mode without lse.
  */
 int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* block_tables,
                         const int32_t* seq_lens, const int32_t* qo_indptr, int32_t max_seq_len,
                         int32_t max_q_len, float bmm1_scale, float bmm2_scale, int causal, void* out,
                         float* lse, void* workspace, size_t workspace_bytes,
                         const mla_decode_dims_t* dims, void* stream, const mla_decode_options_t* opts);
+
+/*
+ * mla_merge_partials -- combine G partial results of the same (row, head)
+ * items, e.g. the sequence shards of DCP mode after an all-to-all:
+ * M = max_g lse_g, w_g = exp(lse_g - M), out = sum_g w_g out_g / sum_g w_g and
+ * lse = M + ln sum_g w_g (vLLM docs, "FlashInferMLAImpl": the natural-log LSE
+ * DCP consumes).  Items whose partials all have lse = -inf get out = 0 and
+ * lse = -inf.  The order of summation is fixed (g ascending).
+ *
+ * outs     device bf16 [G][items][512], 16-byte aligned (items = rows x heads)
+ * lses     device float32 [G][items], 4-byte aligned
+ * out      device bf16 [items][512], 16-byte aligned; written completely
+ * lse      device float32 [items], or NULL
+ * Asynchronous on `stream`; allocates nothing.  Returns MLA_OK,
+ * MLA_ERR_NULL_POINTER, MLA_ERR_MISALIGNED, MLA_ERR_BAD_SHAPE (G < 1 or
+ * items < 1) or MLA_ERR_HIP.
+ */
+int mla_merge_partials(const void* outs, const float* lses, int32_t num_partials, int64_t items, void* out,
+                       float* lse, void* stream);
 
 /*
  * Bytes of workspace mla_decode_paged needs for this shape on the current

@@ -33,6 +33,9 @@ class MlaOptions(ctypes.Structure):
         ("bmm1_scale", ctypes.c_void_p),
         ("bmm2_scale", ctypes.c_void_p),
         ("sinks", ctypes.c_void_p),
+        ("seq_lens_global", ctypes.c_void_p),
+        ("cp_world", ctypes.c_int32),
+        ("cp_rank", ctypes.c_int32),
     ]
 
 
@@ -69,6 +72,8 @@ def load_library():
     lib.mla_decode_paged_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, sz,
                                         ctypes.POINTER(MlaDims), vp, ctypes.POINTER(MlaOptions)]
     lib.mla_decode_paged_ex.restype = ctypes.c_int
+    lib.mla_merge_partials.argtypes = [vp, vp, i32, i64, vp, vp, vp]
+    lib.mla_merge_partials.restype = ctypes.c_int
     lib.mla_decode_paged_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int]
     lib.mla_decode_paged_workspace_size.restype = sz
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -220,12 +225,15 @@ def _device_scalar(name, v, device):
 
 def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_len, *, qo_indptr=None,
            max_seq_len_q=None, out=None, lse=None, return_lse=False, bmm1_scale=1.0, bmm2_scale=1.0,
-           causal=True, sinks=None):
+           causal=True, sinks=None, dcp=None):
     """Batched paged MLA decode.  Returns out, or (out, lse) with return_lse.
 
     bmm1_scale / bmm2_scale: a float, or a one-element float32 device tensor
     read by the kernels at run time (so a captured graph follows updates).
-    sinks: None or a float32 device tensor [H] of per-head sink logits."""
+    sinks: None or a float32 device tensor [H] of per-head sink logits.
+    dcp: None, or (seq_lens_global int32 device [B], cp_world, cp_rank) for the
+    sequence-sharded partial mode (kv_cache / block_tables / seq_lens then hold
+    this rank's rows; needs return_lse); merge the ranks with merge_partials."""
     for name, t in (("query", query), ("kv_cache", kv_cache), ("workspace_buffer", workspace_buffer),
                     ("block_tables", block_tables), ("seq_lens", seq_lens)):
         if not t.is_cuda:
@@ -258,14 +266,44 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
     if sinks is not None and (sinks.dtype != torch.float32 or tuple(sinks.shape) != (H,) or not sinks.is_cuda
                               or not sinks.is_contiguous()):
         raise TypeError(f"sinks must be a contiguous float32 device tensor of shape ({H},)")
-    if b1 is None and b2 is None and sinks is None:
+    if dcp is not None:
+        lens_g, cp_world, cp_rank = dcp
+        if lens_g.dtype != torch.int32 or not lens_g.is_cuda or tuple(lens_g.shape) != tuple(seq_lens.shape):
+            raise TypeError("dcp seq_lens_global must be an int32 device tensor shaped like seq_lens")
+        if not return_lse:
+            raise ValueError("the sequence-sharded mode needs return_lse=True")
+    if b1 is None and b2 is None and sinks is None and dcp is None:
         rc = mla_decode_paged(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q, bmm1_scale,
                               bmm2_scale, causal, out, lse, workspace_buffer, ws_bytes, dims)
     else:
-        opts = MlaOptions(_ptr(b1), _ptr(b2), _ptr(sinks))
+        opts = MlaOptions(_ptr(b1), _ptr(b2), _ptr(sinks), None if dcp is None else _ptr(dcp[0]),
+                          1 if dcp is None else int(dcp[1]), 0 if dcp is None else int(dcp[2]))
         rc = mla_decode_paged_ex(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q,
                                  1.0 if b1 is not None else bmm1_scale, 1.0 if b2 is not None else bmm2_scale,
                                  causal, out, lse, workspace_buffer, ws_bytes, dims, opts)
     if rc != MLA_OK:
         raise RuntimeError(f"mla_decode_paged failed: {mla_status_string(rc)} (status {rc})")
     return (out, lse) if return_lse else out
+
+
+def merge_partials(outs, lses, out=None, lse=None):
+    """Combine G partials of the same items: outs bf16 [G, ..., 512] and lses
+    float32 [G, ...] (e.g. the ranks of a sequence-sharded decode, stacked).
+    Returns (out bf16 [..., 512], lse float32 [...])."""
+    if outs.dtype != torch.bfloat16 or lses.dtype != torch.float32 or not outs.is_cuda or not lses.is_cuda:
+        raise TypeError("outs must be bf16 and lses float32 device tensors")
+    if not outs.is_contiguous() or not lses.is_contiguous():
+        raise ValueError("outs and lses must be contiguous")
+    G = int(outs.shape[0])
+    if tuple(outs.shape[:-1]) != tuple(lses.shape) or outs.shape[-1] != KV_LORA_RANK:
+        raise ValueError("outs must be [G, ..., 512] and lses [G, ...] with matching leading shape")
+    items = lses[0].numel()
+    if out is None:
+        out = torch.empty(tuple(outs.shape[1:]), dtype=torch.bfloat16, device=outs.device)
+    if lse is None:
+        lse = torch.empty(tuple(lses.shape[1:]), dtype=torch.float32, device=outs.device)
+    rc = load_library().mla_merge_partials(outs.data_ptr(), lses.data_ptr(), G, items, out.data_ptr(),
+                                           lse.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if rc != MLA_OK:
+        raise RuntimeError(f"mla_merge_partials failed: {mla_status_string(rc)} (status {rc})")
+    return out, lse

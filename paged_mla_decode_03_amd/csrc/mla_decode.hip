@@ -118,7 +118,22 @@ struct Params {
   const float* bmm1_dev;  // device bmm1_scale (replaces scale_log2 / LOG2E) or null
   const float* bmm2_dev;  // device bmm2_scale (replaces bmm2) or null
   const float* sinks;     // device [heads] sink logits (natural log) or null
+  const int32_t* seq_lens_global;  // sequence-sharded partial mode: global lengths, or null
+  int32_t cp_world;                // ranks sharing each request's rows round-robin
+  int32_t cp_rank;                 // this call's rank: local row j is global position j * cp_world + cp_rank
 };
+
+// Visible local rows of query row qi of a request with q_b rows and L local
+// rows.  Causal rows see global positions below Lg - q_b + qi + 1 (Lg = L
+// unsharded); with rows shared round-robin, rank r holds the global positions
+// r, r + W, ... of which ceil((n - r) / W) lie below n.
+__device__ __forceinline__ int visible_rows(const Params& p, int b, int L, int qb, int qi) {
+  if (!p.causal) return L;
+  if (p.seq_lens_global == nullptr) return L - qb + qi + 1;
+  const int n = p.seq_lens_global[b] - qb + qi + 1;
+  const int r = p.cp_rank, W = p.cp_world;
+  return min(L, n > r ? (n - r + W - 1) / W : 0);
+}
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -864,8 +879,9 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   const int head = valid ? pair - qi * H : 0;
   // visible rows: causal rows see L - q_b + qi + 1; inactive lanes see L (their
   // zero query gives finite logits and their results are discarded)
-  const int n_vis = !valid ? L : (p.causal ? L - qb + qi + 1 : L);
-  const int min_vis = uniform((p.causal && pair0 < npairs) ? L - qb + pair0 / H + 1 : L);
+  const int n_vis = !valid ? L : visible_rows(p, b, L, qb, qi);
+  // (rows see more as qi grows, so the wave's first pair sees the fewest)
+  const int min_vis = uniform(pair0 < npairs ? visible_rows(p, b, L, qb, pair0 / H) : L);
 
   // page ids of the segment, then the first three tiles in flight before the
   // query loads
@@ -1120,12 +1136,12 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int pb = pair / PAIRS_BLOCK;
   const int pl = pair - pb * PAIRS_BLOCK;
   const int C = p.ws_plan[0];
-  const int T = ceil_div(p.seq_lens[b], TILE);
+  const int T = max(0, ceil_div(p.seq_lens[b], TILE));
   const int u = p.ws_plan[3 + p.batch + b] + pb;
   const int U0 = p.ws_plan[2 + b] + pb * T + (u + 1) * p.seg_cost;  // cost position of the unit's first tile
   const int g0 = U0 / C;
   const int g1 = (U0 + T - 1) / C;
-  const int nseg = g1 - g0 + 1;
+  const int nseg = (T > 0) ? g1 - g0 + 1 : 0;  // a request with no rows (a sequence shard may have none) has no segment
   const float* mlb = p.ws_ml + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * 2;  // segment s at + s * PAIRS_BLOCK * 2
   const uint16_t* ob = p.ws_o + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * D_V + 8 * lane;
   // (max, sum) of up to 64 segments at a time, one per lane, all loads in flight together
@@ -1170,7 +1186,10 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   }
   den = wave_sum(den);
   if (sink != -INFINITY) den += __builtin_amdgcn_exp2f(sink - M);
-  const float inv = ((p.bmm2_dev != nullptr) ? *p.bmm2_dev : p.bmm2) / den;
+  // a (row, head) that sees no row (possible only for a sequence shard) gets
+  // out = 0 and lse = -inf
+  const bool empty = !(den > 0.f);
+  const float inv = empty ? 0.f : ((p.bmm2_dev != nullptr) ? *p.bmm2_dev : p.bmm2) / den;
   u32x4 packed;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -1179,7 +1198,58 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
     packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
   *(u32x4*)(p.out + (size_t)item * D_V + 8 * lane) = packed;
-  if (p.lse != nullptr && lane == 0) p.lse[item] = (M + __log2f(den)) * LN2;
+  if (p.lse != nullptr && lane == 0) p.lse[item] = empty ? -INFINITY : (M + __log2f(den)) * LN2;
+}
+
+// Combine G partial results of the same items (the shards of a sequence-
+// sharded decode): M = max_g lse_g, w_g = exp(lse_g - M), out = sum w_g out_g /
+// sum w_g, lse = M + ln sum w_g.  One wave per item, lane l holding dims
+// 8l .. 8l + 8; the lse of up to 64 partials load at once, one per lane.
+__global__ __launch_bounds__(MERGE_THREADS) void mla_merge_partials_kernel(const uint16_t* outs, const float* lses,
+                                                                           int G, int64_t items, uint16_t* out,
+                                                                           float* lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * (MERGE_THREADS / 64) + (threadIdx.x >> 6);
+  if (item >= items) return;
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < G; c0 += 64)
+    if (c0 + lane < G) M = fmaxf(M, lses[(int64_t)(c0 + lane) * items + item]);
+  M = wave_max(M);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float den = 0.f;
+  if (M != -INFINITY) {
+    for (int c0 = 0; c0 < G; c0 += 64) {
+      float wl = 0.f;
+      if (c0 + lane < G) {
+        const float l = lses[(int64_t)(c0 + lane) * items + item];
+        wl = (l == -INFINITY) ? 0.f : __expf(l - M);
+        den += wl;
+      }
+      const int cn = min(64, G - c0);
+      for (int g = 0; g < cn; ++g) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), g));
+        if (w == 0.f) continue;  // wave-uniform: an empty partial adds nothing
+        const u32x4 o = *(const u32x4*)(outs + ((int64_t)(c0 + g) * items + item) * D_V + 8 * lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += w * __uint_as_float(o[e] << 16);
+          acc[2 * e + 1] += w * __uint_as_float(o[e] & 0xffff0000u);
+        }
+      }
+    }
+    den = wave_sum(den);
+  }
+  const bool empty = !(den > 0.f);
+  const float inv = empty ? 0.f : 1.f / den;
+  u32x4 packed;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 lo = (__bf16)(acc[2 * e] * inv);
+    const __bf16 hi = (__bf16)(acc[2 * e + 1] * inv);
+    packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  *(u32x4*)(out + item * D_V + 8 * lane) = packed;
+  if (lse != nullptr && lane == 0) lse[item] = empty ? -INFINITY : M + __logf(den);
 }
 
 // Conversion check: the exact fp8 -> bf16 widening the decode kernel uses, on
@@ -1304,9 +1374,12 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
                         float bmm2_scale, int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
                         const mla_decode_dims_t* dims, void* stream, const mla_decode_options_t* opts) {
   if (!q || !kv_cache || !block_tables || !seq_lens || !out || !workspace || !dims) return MLA_ERR_NULL_POINTER;
-  if (opts != nullptr &&
-      (((uintptr_t)opts->bmm1_scale | (uintptr_t)opts->bmm2_scale | (uintptr_t)opts->sinks) & 3))
+  if (opts != nullptr && (((uintptr_t)opts->bmm1_scale | (uintptr_t)opts->bmm2_scale | (uintptr_t)opts->sinks |
+                            (uintptr_t)opts->seq_lens_global) & 3))
     return MLA_ERR_MISALIGNED;
+  const bool dcp = opts != nullptr && opts->seq_lens_global != nullptr;
+  if (dcp && (opts->cp_world < 1 || opts->cp_rank < 0 || opts->cp_rank >= opts->cp_world)) return MLA_ERR_BAD_SHAPE;
+  if (dcp && lse == nullptr) return MLA_ERR_NULL_POINTER;
   const int v = validate(dims, max_seq_len, max_q_len, qo_indptr != nullptr);
   if (v != MLA_OK) return v;
   if (((uintptr_t)q | (uintptr_t)kv_cache | (uintptr_t)out | (uintptr_t)workspace) & 15) return MLA_ERR_MISALIGNED;
@@ -1342,6 +1415,9 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   p.bmm1_dev = opts ? opts->bmm1_scale : nullptr;
   p.bmm2_dev = opts ? opts->bmm2_scale : nullptr;
   p.sinks = opts ? opts->sinks : nullptr;
+  p.seq_lens_global = dcp ? opts->seq_lens_global : nullptr;
+  p.cp_world = dcp ? opts->cp_world : 1;
+  p.cp_rank = dcp ? opts->cp_rank : 0;
 
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = dims->kv_dtype == MLA_KV_FP8_E4M3FN;
@@ -1356,6 +1432,19 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   if (ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev1, s);
   const int items = dims->total_q * dims->num_heads;
   hipLaunchKernelGGL(mla_merge_kernel, dim3((items + 3) / 4), dim3(MERGE_THREADS), 0, s, p);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_merge_partials(const void* outs, const float* lses, int32_t num_partials, int64_t items, void* out,
+                       float* lse, void* stream) {
+  if (!outs || !lses || !out) return MLA_ERR_NULL_POINTER;
+  if (num_partials < 1 || items < 1) return MLA_ERR_BAD_SHAPE;
+  if ((((uintptr_t)outs | (uintptr_t)out) & 15) || (((uintptr_t)lses | (uintptr_t)lse) & 3)) return MLA_ERR_MISALIGNED;
+  const int64_t blocks = (items + MERGE_THREADS / 64 - 1) / (MERGE_THREADS / 64);
+  if (blocks > 0x7fffffff) return MLA_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(mla_merge_partials_kernel, dim3((unsigned)blocks), dim3(MERGE_THREADS), 0, (hipStream_t)stream,
+                     (const uint16_t*)outs, lses, (int)num_partials, items, (uint16_t*)out, lse);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -91,7 +91,7 @@ MISALIGNED = 6
 
 def test_options_struct_and_misaligned_option_pointers():
     # three pointers, in header order
-    assert ctypes.sizeof(binding.MlaOptions) == 24
+    assert ctypes.sizeof(binding.MlaOptions) == 40
     assert binding.MlaOptions.sinks.offset == 16
     for field in ("bmm1_scale", "bmm2_scale", "sinks"):
         opts = binding.MlaOptions(None, None, None)
@@ -104,3 +104,21 @@ def test_options_struct_and_misaligned_option_pointers():
     rc_ex = binding.mla_decode_paged_ex(FAKE, FAKE, FAKE, FAKE, None, 128, 1, 1.0, 1.0, True, FAKE, None, FAKE,
                                         1 << 30, bad, None, stream=0)
     assert rc_ex == _call(bad)
+
+
+def test_dcp_options_and_merge_partials_reject_bad_arguments():
+    def ex(opts, lse=FAKE):
+        return binding.mla_decode_paged_ex(FAKE, FAKE, FAKE, FAKE, None, 128, 1, 1.0, 1.0, True, FAKE, lse, FAKE,
+                                           1 << 30, _dims(), opts, stream=0)
+    BAD_SHAPE, NULL = 10, 1
+    assert ex(binding.MlaOptions(None, None, None, FAKE, 0, 0)) == BAD_SHAPE      # cp_world < 1
+    assert ex(binding.MlaOptions(None, None, None, FAKE, 4, 4)) == BAD_SHAPE      # cp_rank >= cp_world
+    assert ex(binding.MlaOptions(None, None, None, FAKE, 4, -1)) == BAD_SHAPE     # cp_rank < 0
+    assert ex(binding.MlaOptions(None, None, None, FAKE, 2, 1), lse=None) == NULL  # partial mode needs lse
+    assert ex(binding.MlaOptions(None, None, None, FAKE + 2, 2, 1)) == MISALIGNED
+    lib = binding.load_library()
+    assert lib.mla_merge_partials(None, FAKE, 2, 16, FAKE, None, None) == NULL
+    assert lib.mla_merge_partials(FAKE, FAKE, 0, 16, FAKE, None, None) == BAD_SHAPE
+    assert lib.mla_merge_partials(FAKE, FAKE, 2, 0, FAKE, None, None) == BAD_SHAPE
+    assert lib.mla_merge_partials(FAKE + 8, FAKE, 2, 16, FAKE, None, None) == MISALIGNED
+    assert lib.mla_merge_partials(FAKE, FAKE + 2, 2, 16, FAKE, None, None) == MISALIGNED
