@@ -236,6 +236,10 @@ def reference_dcp_partial(problem, rank, world):
     since each partial already carries it) gives the full decode (vLLM docs,
     "FlashInferMLAImpl", forward_mqa: DCP passes cp_world, cp_rank and the
     global causal lengths and consumes the natural-log LSE).
+
+    Sinks, if any, belong to rank 0's partial alone: a sink is one softmax
+    term per (row, head), so the merged result counts it once.  A rank-0 row
+    that sees no rows then has out = 0 and lse = sink.
     """
     H = problem.num_heads
     R = problem.q_bits.shape[0]
@@ -247,13 +251,18 @@ def reference_dcp_partial(problem, rank, world):
         S, visible = _masked_logits(problem, b, Kb)
         mine = (np.arange(L) % world) == rank
         visible = visible & mine[None, :]
-        any_vis = visible.any(axis=1)
         S = np.where(visible, S, -np.inf)
-        m = np.where(any_vis, S.max(axis=1), 0.0)
+        if problem.sinks is not None and rank == 0:
+            # the sink as one more logit, attached to a zero value row
+            sink = np.tile(np.asarray(problem.sinks, dtype=np.float64), q_b)  # row index = i*H + h
+        else:
+            sink = np.full(S.shape[0], -np.inf)
+        any_term = visible.any(axis=1) | (sink > -np.inf)
+        m = np.where(any_term, np.maximum(S.max(axis=1), sink), 0.0)
         e = np.where(visible, np.exp(S - m[:, None]), 0.0)
-        Z = e.sum(axis=1)
-        Zs = np.where(any_vis, Z, 1.0)
+        Z = e.sum(axis=1) + np.where(sink > -np.inf, np.exp(sink - m), 0.0)
+        Zs = np.where(any_term, Z, 1.0)
         O = (e / Zs[:, None]) @ Kb[:, :D_LATENT] * float(problem.bmm2_scale)
         out[r_b:r_b + q_b] = O.reshape(q_b, H, D_LATENT)
-        lse[r_b:r_b + q_b] = np.where(any_vis, m + np.log(Zs), -np.inf).reshape(q_b, H)
+        lse[r_b:r_b + q_b] = np.where(any_term, m + np.log(Zs), -np.inf).reshape(q_b, H)
     return out, lse

@@ -290,6 +290,56 @@ def test_dcp_partials_merge_to_the_full_decode(world):
                 assert np.all(parts[r][1][0] == -np.inf) and np.all(parts[r][0][0] == 0.0)
 
 
+@pytest.mark.parametrize("world", [2, 5])
+def test_dcp_sinks_ride_on_rank_zero(world):
+    """With sinks, rank 0's partial carries them and the merge counts each
+    sink once, reproducing the unsharded decode with sinks; a rank-0 row that
+    sees none of its own rows reports out = 0 and lse = sink."""
+    rng = np.random.default_rng(26)
+    H = 16
+    sinks = rng.uniform(-3.0, 6.0, H)
+    q, ks = random_dense(rng, 2, H, [3, 1], [3, 77])
+    prob = build_paged(q, ks, 32, rng=rng, q_lens=[3, 1], packed=True, bmm1=0.09, bmm2=1.2, causal=True)
+    prob.sinks = sinks
+    full_o, full_l = oracle.reference_decode(prob)
+    parts = [oracle.reference_dcp_partial(prob, r, world) for r in range(world)]
+    mo, ml = oracle.merge_partials(parts, 1.0)
+    np.testing.assert_allclose(mo, full_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ml, full_l, rtol=1e-12, atol=1e-13)
+    for r in range(1, world):
+        # the other ranks are the sink-free partials
+        prob.sinks = None
+        o_r, l_r = oracle.reference_dcp_partial(prob, r, world)
+        prob.sinks = sinks
+        np.testing.assert_array_equal(parts[r][1], l_r)
+        np.testing.assert_array_equal(parts[r][0], o_r)
+
+
+def test_dcp_sink_closed_forms():
+    """q = 3, L = 3, causal, two ranks: row i sees global positions 0..i;
+    rank 0 holds positions 0 and 2, rank 1 holds position 1.  Rank 0's row 0
+    is a logistic gate between position 0 and the sink; rank 1's row 0 has
+    nothing (out = 0, lse = -inf); rank 1's row 1 is position 1 alone."""
+    rng = np.random.default_rng(27)
+    H = 16
+    sinks = rng.uniform(-2.0, 2.0, H)
+    q, ks = random_dense(rng, 1, H, [3], [3])
+    prob = build_paged(q, ks, 32, rng=rng, q_lens=[3], packed=True, bmm1=0.1, bmm2=0.8, causal=True)
+    prob.sinks = sinks
+    o0, l0 = oracle.reference_dcp_partial(prob, 0, 2)
+    o1, l1 = oracle.reference_dcp_partial(prob, 1, 2)
+    K = ks[0]
+    for h in range(H):
+        s00 = 0.1 * float(q[0, h] @ K[0])
+        gate = 1.0 / (1.0 + math.exp(sinks[h] - s00))
+        np.testing.assert_allclose(o0[0, h], 0.8 * gate * K[0, :512], rtol=1e-12, atol=1e-300)
+        assert abs(l0[0, h] - np.logaddexp(s00, sinks[h])) < 1e-12
+        assert l1[0, h] == -np.inf and np.all(o1[0, h] == 0.0)
+        s11 = 0.1 * float(q[1, h] @ K[1])
+        np.testing.assert_allclose(o1[1, h], 0.8 * K[1, :512], rtol=1e-12, atol=1e-300)
+        assert abs(l1[1, h] - s11) < 1e-12
+
+
 def test_dcp_single_rank_is_the_full_decode():
     rng = np.random.default_rng(25)
     q, ks = random_dense(rng, 2, 16, [2, 2], [33, 80])
