@@ -142,6 +142,10 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
  *             local rows and ln of their exponent sum; a (row, head) with no
  *             visible local row gets out = 0 and lse = -inf.  mla_merge_partials
  *             combines the ranks' partials (lse is required in this mode).
+ *             Sinks, when given, enter rank 0's partial only (on other ranks
+ *             they are ignored), so the merge counts each sink once; a rank-0
+ *             (row, head) with no visible local row then has out = 0 and
+ *             lse = sinks[h].
  * cp_world, cp_rank
  *             1 <= cp_world, 0 <= cp_rank < cp_world; read only in DCP mode.
  * All pointers must be 4-byte aligned and stay valid until the enqueued work

@@ -233,7 +233,8 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
     sinks: None or a float32 device tensor [H] of per-head sink logits.
     dcp: None, or (seq_lens_global int32 device [B], cp_world, cp_rank) for the
     sequence-sharded partial mode (kv_cache / block_tables / seq_lens then hold
-    this rank's rows; needs return_lse); merge the ranks with merge_partials."""
+    this rank's rows; needs return_lse); merge the ranks with merge_partials.
+    Sinks given with dcp enter rank 0's partial only."""
     for name, t in (("query", query), ("kv_cache", kv_cache), ("workspace_buffer", workspace_buffer),
                     ("block_tables", block_tables), ("seq_lens", seq_lens)):
         if not t.is_cuda:

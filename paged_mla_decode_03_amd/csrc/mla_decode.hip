@@ -1414,7 +1414,9 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   p.seg_cost = g_seg_cost.load(std::memory_order_relaxed);
   p.bmm1_dev = opts ? opts->bmm1_scale : nullptr;
   p.bmm2_dev = opts ? opts->bmm2_scale : nullptr;
-  p.sinks = opts ? opts->sinks : nullptr;
+  // a sink is one softmax term per (row, head): in a sequence-sharded decode
+  // rank 0's partial carries it, so merging the ranks counts it once
+  p.sinks = (opts != nullptr && !(dcp && opts->cp_rank != 0)) ? opts->sinks : nullptr;
   p.seq_lens_global = dcp ? opts->seq_lens_global : nullptr;
   p.cp_world = dcp ? opts->cp_world : 1;
   p.cp_rank = dcp ? opts->cp_rank : 0;

@@ -65,9 +65,7 @@ def _check_partial(got_o, got_l, ref_o, ref_l, what):
         check_close(got_l[~empty], ref_l[~empty], f"{what} lse")
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
-@pytest.mark.parametrize("world", [2, 3, 8])
-def test_sequence_shards_match_oracle_and_merge_to_full(kv_dtype, world):
+def _run_shards(kv_dtype, world, with_sinks):
     fp8 = kv_dtype != "bf16"
     # short requests too, so that some ranks hold no visible row (or no row) of them
     w = make_workload("dcp", seed=50 + world, seq_lens=[3, 5, 40, 333, 1200], num_heads=32, q_len=3,
@@ -76,6 +74,12 @@ def test_sequence_shards_match_oracle_and_merge_to_full(kv_dtype, world):
                       causal=True, want_lse=True)
     prob = oracle.MlaProblem(**w.oracle_problem_kwargs())
     B, H, R = w.batch, w.num_heads, w.total_q
+    sinks = None
+    if with_sinks:
+        # logits around the scale of the scores, some dominating
+        sv = np.random.default_rng(70 + world).uniform(-4.0, 8.0, H).astype(np.float32)
+        prob.sinks = sv.astype(np.float64)
+        sinks = torch.from_numpy(sv).cuda()
     q = torch.from_numpy(w.q_bits).view(torch.bfloat16).cuda().view(B, w.q_len_fixed, H, 576)
     lens_g = torch.from_numpy(w.seq_lens.astype(np.int32)).cuda()
     outs, lses = [], []
@@ -87,7 +91,7 @@ def test_sequence_shards_match_oracle_and_merge_to_full(kv_dtype, world):
         ws = torch.empty(binding.workspace_bytes_for(q, kv, bt_t, lens_t, max_len, return_lse=True),
                          dtype=torch.uint8, device="cuda")
         o, l = binding.decode(q, kv, ws, bt_t, lens_t, max_len, return_lse=True, bmm1_scale=w.bmm1_scale,
-                              bmm2_scale=w.bmm2_scale, causal=True, dcp=(lens_g, world, r))
+                              bmm2_scale=w.bmm2_scale, causal=True, dcp=(lens_g, world, r), sinks=sinks)
         torch.cuda.synchronize()
         ref_o, ref_l = oracle.reference_dcp_partial(prob, r, world)
         _check_partial(o.float().reshape(R, H, 512).cpu().numpy(), l.reshape(R, H).cpu().numpy(), ref_o, ref_l,
@@ -99,6 +103,18 @@ def test_sequence_shards_match_oracle_and_merge_to_full(kv_dtype, world):
     full_o, full_l = oracle.reference_decode(prob)
     check_close(mo.float().reshape(R, H, 512).cpu().numpy(), full_o, "merged out")
     check_close(ml.reshape(R, H).cpu().numpy(), full_l, "merged lse")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("world", [2, 3, 8])
+def test_sequence_shards_match_oracle_and_merge_to_full(kv_dtype, world):
+    _run_shards(kv_dtype, world, with_sinks=False)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_sequence_shards_with_sinks(kv_dtype):
+    """Rank 0 carries the sinks; the merged ranks equal the full decode with sinks."""
+    _run_shards(kv_dtype, 3, with_sinks=True)
 
 
 def test_single_rank_partial_equals_plain_decode():
