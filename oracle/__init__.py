@@ -16,13 +16,16 @@ Sources (web pages on the method; cited by title and section):
     ragged query-offset array.
   * FlashInfer PR #1248, "update cubins for dynamic scale factor interface and
     one-copy kvcache on trtllm-gen mla" -- bmm1/bmm2 scale derivation.
+  * FlashInfer issue #3131 -- the trtllm_batch_decode_with_kv_cache_mla and
+    trtllm_paged_attention_decode signatures carry sparse_mla_top_k (the
+    sparse top-k reading is in oracle/sparse.py).
   * vLLM docs, "FlashInferMLAImpl" -- forward_mqa (scale folding for
     quantized KV, natural-log LSE, ragged/uniform query branches) and
     _flattened_decode_metadata.
 
 Every function here is pinned by tests that do not re-type its formula:
 closed forms, invariants, brute force and a library attention routine (see
-tests/test_oracle_pins.py).  No function is parity-unpinned.
+tests/test_oracle_pins.py, tests/test_oracle_sparse.py).  No function is parity-unpinned.
 """
 
 from .formats import bf16_bits_to_f64, e4m3fn_bits_to_f64, e4m3fn_table
@@ -35,6 +38,7 @@ from .mla import (
     reference_dcp_partial,
     merge_partials,
 )
+from .sparse import reference_sparse_decode
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -47,4 +51,5 @@ __all__ = [
     "reference_partial",
     "reference_dcp_partial",
     "merge_partials",
+    "reference_sparse_decode",
 ]
