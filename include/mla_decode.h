@@ -52,8 +52,12 @@ enum {
 
 enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3FN = 1 };
 
-/* Largest batch one launch accepts (the work plan lives in LDS). */
+/* Largest batch one launch accepts (the work plan lives in LDS); in the
+   sparse top-k layout, the largest number of query rows. */
 #define MLA_MAX_BATCH 1024
+
+/* Largest sparse top-k list length. */
+#define MLA_MAX_TOP_K (1 << 20)
 
 /* Static shape of a launch.  All fields are host integers. */
 typedef struct mla_decode_dims {
@@ -148,6 +152,25 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
  *             lse = sinks[h].
  * cp_world, cp_rank
  *             1 <= cp_world, 0 <= cp_rank < cp_world; read only in DCP mode.
+ * sparse_top_k
+ *             0: the paged layout above.  K > 0: sparse top-k layout
+ *             (FlashInfer issue #3131: the trtllm_batch_decode_with_kv_cache_mla
+ *             and trtllm_paged_attention_decode signatures carry
+ *             sparse_mla_top_k; the pages give no index layout, so this is the
+ *             library's reading).  block_tables is then a device int32 array
+ *             [total_q, block_table_stride] (stride >= K)
+ *             whose row r lists, in its first K entries, the cache rows query
+ *             row r attends to: entry e >= 0 is cache row e of the cache seen as
+ *             [num_pages * page_size, 576] (page e / page_size, slot
+ *             e % page_size; e < num_pages * page_size is the caller's contract,
+ *             unchecked); a negative entry is empty.  Every head of row r
+ *             attends to exactly the listed rows (a repeated entry counts once
+ *             per listing); no causal or length mask applies, and seq_lens,
+ *             qo_indptr, max_seq_len, max_q_len and causal are not read (seq_lens
+ *             may be NULL).  A (row, head) with no live entry gets out = 0 and
+ *             lse = -inf (lse = sinks[h] with a sink).  total_q <= MLA_MAX_BATCH,
+ *             K <= MLA_MAX_TOP_K; not combinable with DCP mode.  The workspace
+ *             size comes from mla_decode_paged_ex_workspace_size().
  * All pointers must be 4-byte aligned and stay valid until the enqueued work
  * completes; the library only reads them.
  */
@@ -158,6 +181,7 @@ typedef struct {
   const int32_t* seq_lens_global;
   int32_t cp_world;
   int32_t cp_rank;
+  int32_t sparse_top_k;
 } mla_decode_options_t;
 
 /*
@@ -165,7 +189,10 @@ typedef struct {
  * Arguments as mla_decode_paged; opts may be NULL (then identical to it).
  * Same workspace, same errors, plus MLA_ERR_MISALIGNED for an option pointer
  * that is not 4-byte aligned, MLA_ERR_BAD_SHAPE for cp_world < 1 or cp_rank
- * outside [0, cp_world), and MLA_ERR_NULL_POINTER for DCP mode without lse.
+ * outside [0, cp_world), a negative sparse_top_k, sparse_top_k above
+ * MLA_MAX_TOP_K, total_q above MLA_MAX_BATCH in the sparse layout, or DCP and
+ * sparse together, MLA_ERR_BAD_BLOCK_TABLE for block_table_stride <
+ * sparse_top_k, and MLA_ERR_NULL_POINTER for DCP mode without lse.
  */
 int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* block_tables,
                         const int32_t* seq_lens, const int32_t* qo_indptr, int32_t max_seq_len,
@@ -200,6 +227,15 @@ int mla_merge_partials(const void* outs, const float* lses, int32_t num_partials
  */
 size_t mla_decode_paged_workspace_size(const mla_decode_dims_t* dims, int32_t max_seq_len,
                                        int32_t max_q_len, int want_lse);
+
+/*
+ * Bytes of workspace mla_decode_paged_ex needs with these options: the same as
+ * mla_decode_paged_workspace_size() unless opts selects the sparse top-k
+ * layout, where the size depends on dims (total_q, num_heads) and
+ * opts->sparse_top_k only.  Returns 0 for a shape the call would reject.
+ */
+size_t mla_decode_paged_ex_workspace_size(const mla_decode_dims_t* dims, int32_t max_seq_len, int32_t max_q_len,
+                                          int want_lse, const mla_decode_options_t* opts);
 
 /* Static, NUL-terminated description of a status code. */
 const char* mla_status_string(int status);

@@ -36,6 +36,7 @@ class MlaOptions(ctypes.Structure):
         ("seq_lens_global", ctypes.c_void_p),
         ("cp_world", ctypes.c_int32),
         ("cp_rank", ctypes.c_int32),
+        ("sparse_top_k", ctypes.c_int32),
     ]
 
 
@@ -76,6 +77,9 @@ def load_library():
     lib.mla_merge_partials.restype = ctypes.c_int
     lib.mla_decode_paged_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int]
     lib.mla_decode_paged_workspace_size.restype = sz
+    lib.mla_decode_paged_ex_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int,
+                                                       ctypes.POINTER(MlaOptions)]
+    lib.mla_decode_paged_ex_workspace_size.restype = sz
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_decode_internal_set_grid_override.argtypes = [i32]
@@ -111,6 +115,12 @@ def make_dims(*, batch, num_heads, q_len_fixed, total_q, page_size, num_pages, b
 def mla_decode_paged_workspace_size(dims, max_seq_len, max_q_len, want_lse=False):
     return int(load_library().mla_decode_paged_workspace_size(ctypes.byref(dims), int(max_seq_len),
                                                              int(max_q_len), int(bool(want_lse))))
+
+
+def mla_decode_paged_ex_workspace_size(dims, max_seq_len, max_q_len, want_lse, opts):
+    return int(load_library().mla_decode_paged_ex_workspace_size(
+        ctypes.byref(dims), int(max_seq_len), int(max_q_len), int(bool(want_lse)),
+        None if opts is None else ctypes.byref(opts)))
 
 
 def mla_decode_paged(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q_len, bmm1_scale,
@@ -278,12 +288,88 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
                               bmm2_scale, causal, out, lse, workspace_buffer, ws_bytes, dims)
     else:
         opts = MlaOptions(_ptr(b1), _ptr(b2), _ptr(sinks), None if dcp is None else _ptr(dcp[0]),
-                          1 if dcp is None else int(dcp[1]), 0 if dcp is None else int(dcp[2]))
+                          1 if dcp is None else int(dcp[1]), 0 if dcp is None else int(dcp[2]), 0)
         rc = mla_decode_paged_ex(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q,
                                  1.0 if b1 is not None else bmm1_scale, 1.0 if b2 is not None else bmm2_scale,
                                  causal, out, lse, workspace_buffer, ws_bytes, dims, opts)
     if rc != MLA_OK:
         raise RuntimeError(f"mla_decode_paged failed: {mla_status_string(rc)} (status {rc})")
+    return (out, lse) if return_lse else out
+
+
+def _sparse_dims(query, kv_cache, indices):
+    if kv_cache.dim() == 4:
+        if kv_cache.shape[1] != 1:
+            raise ValueError("rank-4 kv_cache must be [pages, 1, page_size, 576]")
+        kv_cache = kv_cache.squeeze(1)
+    if kv_cache.dim() != 3 or kv_cache.shape[-1] != D_QK:
+        raise ValueError("kv_cache must be [pages, page_size, 576]")
+    if query.dim() not in (3, 4) or query.shape[-1] != D_QK:
+        raise ValueError("query must be [rows, H, 576] or [B, SQ, H, 576]")
+    H = int(query.shape[-2])
+    R = query.numel() // (H * D_QK)
+    if indices.dim() != 2 or int(indices.shape[0]) != R:
+        raise ValueError(f"indices must be [{R}, top_k] (one list per query row)")
+    dims = make_dims(batch=R, num_heads=H, q_len_fixed=1, total_q=R, page_size=int(kv_cache.shape[1]),
+                     num_pages=int(kv_cache.shape[0]), block_table_stride=int(indices.shape[1]),
+                     kv_dtype=_kv_code(kv_cache.dtype))
+    return dims, R, H
+
+
+def sparse_workspace_bytes_for(query, kv_cache, indices, *, top_k=None, return_lse=False):
+    dims, _, _ = _sparse_dims(query, kv_cache, indices)
+    k = int(indices.shape[1]) if top_k is None else int(top_k)
+    opts = MlaOptions(None, None, None, None, 1, 0, k)
+    n = mla_decode_paged_ex_workspace_size(dims, 1, 1, return_lse, opts)
+    if n == 0:
+        raise ValueError("shape rejected by the library (see mla_decode_paged_ex status codes)")
+    return n
+
+
+def decode_sparse(query, kv_cache, workspace_buffer, indices, *, top_k=None, out=None, lse=None, return_lse=False,
+                  bmm1_scale=1.0, bmm2_scale=1.0, sinks=None):
+    """Sparse top-k MLA decode: every head of query row r attends to the cache
+    rows listed in indices[r, :top_k] (int32 flat token ids page * page_size +
+    slot; negative = empty).  The indices go to the C library as its
+    block_tables with mla_decode_options_t.sparse_top_k = top_k (default: the
+    row width).  Scales and sinks as in decode().  Returns out, or (out, lse)."""
+    for name, t in (("query", query), ("kv_cache", kv_cache), ("workspace_buffer", workspace_buffer),
+                    ("indices", indices)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if query.dtype != torch.bfloat16:
+        raise TypeError("query must be bfloat16")
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32")
+    dims, R, H = _sparse_dims(query, kv_cache, indices)
+    k = int(indices.shape[1]) if top_k is None else int(top_k)
+    out_shape = tuple(query.shape[:-1]) + (KV_LORA_RANK,)
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.bfloat16, device=query.device)
+    elif tuple(out.shape) != out_shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {out_shape}")
+    if return_lse:
+        lse_shape = tuple(query.shape[:-1])
+        if lse is None:
+            lse = torch.empty(lse_shape, dtype=torch.float32, device=query.device)
+        elif tuple(lse.shape) != lse_shape or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError(f"lse must be a contiguous float32 tensor of shape {lse_shape}")
+    else:
+        lse = None
+    b1 = _device_scalar("bmm1_scale", bmm1_scale, query.device)
+    b2 = _device_scalar("bmm2_scale", bmm2_scale, query.device)
+    if sinks is not None and (sinks.dtype != torch.float32 or tuple(sinks.shape) != (H,) or not sinks.is_cuda
+                              or not sinks.is_contiguous()):
+        raise TypeError(f"sinks must be a contiguous float32 device tensor of shape ({H},)")
+    opts = MlaOptions(_ptr(b1), _ptr(b2), _ptr(sinks), None, 1, 0, k)
+    ws_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
+    rc = mla_decode_paged_ex(query, kv_cache, indices, None, None, 1, 1, 1.0 if b1 is not None else bmm1_scale,
+                             1.0 if b2 is not None else bmm2_scale, False, out, lse, workspace_buffer, ws_bytes,
+                             dims, opts)
+    if rc != MLA_OK:
+        raise RuntimeError(f"mla_decode_paged_ex (sparse) failed: {mla_status_string(rc)} (status {rc})")
     return (out, lse) if return_lse else out
 
 

@@ -65,7 +65,12 @@ constexpr int PLAN_INTS = MLA_MAX_BATCH + 1;
 constexpr int PSLOT_OFF = NBUF * TILEB;        // P exchange: [4 waves][2 KB] bf16 P of a tile
 constexpr int PSLOT_BYTES = 2048;
 constexpr int FLAGS_OFF = PSLOT_OFF + WAVES * PSLOT_BYTES;  // end-of-segment flags
-constexpr int LDS_BYTES = FLAGS_OFF + 64;
+// Sparse top-k lists: each wave's 8 entries of a tile, in a ring of IDX_SLOTS
+// tiles, and one byte per wave and tile slot marking the live rows.
+constexpr int IDX_SLOTS = 4;
+constexpr int IDX_OFF = FLAGS_OFF + 64;
+constexpr int VMASK_OFF = IDX_OFF + IDX_SLOTS * WAVES * 32;
+constexpr int LDS_BYTES = VMASK_OFF + IDX_SLOTS * 4;
 // The work-plan scan (prologue only) aliases the tile buffers while they are idle.
 constexpr int PLAN_SCRATCH_OFF = 0;
 constexpr int UNIT_SCRATCH_OFF = PLAN_INTS * 4 + 60;
@@ -81,6 +86,7 @@ constexpr int SEG_COST_DEFAULT = 8;
 constexpr int SEG_COST_MAX = 256;
 
 static_assert(LDS_BYTES <= 163840, "LDS budget");
+static_assert(IDX_SLOTS == 4, "a segment start fetches four tiles' list entries, one ring slot each");
 static_assert(PAIRS_BLOCK * D_V * 2 <= NBUF * TILEB, "the O block is staged in the tile buffers");
 static_assert(SCAN_SCRATCH_OFF + 2 * THREADS * 4 <= TILEB, "plan scratch fits in one tile buffer");
 
@@ -121,6 +127,7 @@ struct Params {
   const int32_t* seq_lens_global;  // sequence-sharded partial mode: global lengths, or null
   int32_t cp_world;                // ranks sharing each request's rows round-robin
   int32_t cp_rank;                 // this call's rank: local row j is global position j * cp_world + cp_rank
+  int32_t sparse_k;                // top-k list length (sparse layout: one query row per request), or 0
 };
 
 // Visible local rows of query row qi of a request with q_b rows and L local
@@ -307,7 +314,10 @@ __device__ __forceinline__ void lds_zero16(uint8_t* smem, uint32_t off) {
 // 128-pair units and 32-row tiles of request b (lengths outside the documented
 // ranges count as empty, so that the work walk always advances)
 __device__ __forceinline__ int request_units(const Params& p, int qb) { return max(0, ceil_div(qb * p.heads, PAIRS_BLOCK)); }
-__device__ __forceinline__ int request_tiles(const Params& p, int b) { return max(0, ceil_div(p.seq_lens[b], TILE)); }
+// Rows of request b: its length, or the top-k list length in the sparse
+// layout (where every query row is a request of its own).
+__device__ __forceinline__ int req_len(const Params& p, int b) { return p.sparse_k > 0 ? p.sparse_k : p.seq_lens[b]; }
+__device__ __forceinline__ int request_tiles(const Params& p, int b) { return max(0, ceil_div(req_len(p, b), TILE)); }
 
 __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* scan) {
   const int tid = threadIdx.x;
@@ -425,6 +435,21 @@ __device__ __forceinline__ TileLoad prepare_tile(const Params& p, uint8_t* smem,
   const int row0 = t * TILE + 8 * w;
   const uint32_t lds0 = lds_addr(smem);
   TileLoad tl{nullptr, 0u, 0u};
+  {
+    // the common case in straight-line scalar code: a full share whose page id
+    // is in the window
+    constexpr int WIN = page_window<FP8>();
+    const int pi = uniform(row0 / PS - pw.base);
+    if (row0 + 8 <= L && pi < WIN) {
+      const int e_lo = __builtin_amdgcn_readlane(pw.lo, pi & 63);
+      const int e_hi = (WIN > 64) ? __builtin_amdgcn_readlane(pw.hi, pi & 63) : e_lo;
+      const int page = uniform(pi < 64 ? e_lo : e_hi);
+      const size_t rowb = FP8 ? ROWB_FP8 : ROWB_BF16;
+      const uint8_t* pg = p.kv + ((size_t)page * PS + (row0 % PS)) * rowb;
+      if (!FP8) return TileLoad{pg, lds0 + buf + 8 * w * 1024, lds0 + buf + ROPE_OFF_BF16 + 8 * w * 128};
+      return TileLoad{pg, lds0 + buf + 8 * w * 512, lds0 + buf + ROPE_OFF_FP8 + 8 * w * 64};
+    }
+  }
   if (!FP8) {
     const uint32_t lat = buf + 8 * w * 1024;
     const uint32_t rope = buf + ROPE_OFF_BF16 + 8 * w * 128;
@@ -538,6 +563,137 @@ template <bool FP8, int PS>
 __device__ __forceinline__ void issue_tile(const Params& p, uint8_t* smem, uint32_t buf, int b, int L, int t,
                                            PageWin& pw) {
   issue_tile_share<FP8>(prepare_tile<FP8, PS>(p, smem, buf, b, L, t, pw));
+}
+
+// ---------------------------------------------------------------- sparse top-k gather
+//
+// In the sparse layout (FlashInfer's sparse_mla_top_k; the list layout is this
+// library's reading) a unit is one query row and its tile t holds entries
+// 32t .. 32t + 31 of the row's list: entry e >= 0 is cache row e, at
+// kv + e * row bytes (the pages are contiguous, so that is page e / page_size,
+// slot e % page_size); a negative entry, or a position past top-k, is an empty
+// row.  A wave's share of a tile (rows 8w .. 8w + 7) needs its 8 entries
+// before its DMA can be issued: one 4-byte-per-lane LDS DMA fetches them into
+// a ring two tiles ahead, in the same vmcnt stream as the tiles.  Every share
+// issues the same instructions (an empty row's with no lanes, its LDS row
+// zero-filled) and publishes one byte of live-row bits for the softmax.
+
+// One DMA instruction of 4 bytes per lane (wave-uniform base + lane offset)
+// under a lane mask.  With no lanes it still issues and counts in vmcnt; exec
+// is restored inside the asm, and the s_nop covers the wait states an exec
+// write owes later lane-crossing VALU instructions.
+__device__ __forceinline__ void dma4_m(const void* sbase, uint32_t voff, uint32_t lds_wave_base, uint64_t lanes) {
+  const uint64_t sb = (uint64_t)(uintptr_t)sbase;
+  const uint64_t sbu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sb) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sb >> 32)) << 32);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)lanes);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(lanes >> 32));
+  uint64_t save;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b32 exec_lo, exec_lo, %4\n\t"
+      "s_and_b32 exec_hi, exec_hi, %5\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b64 exec, %0\n\t"
+      "s_nop 4"
+      : "=&s"(save)
+      : "v"(voff), "s"((const void*)(uintptr_t)sbu), "s"(m0), "s"(lo), "s"(hi)
+      : "memory");
+}
+
+// One 16-byte-per-lane DMA instruction from per-lane 64-bit addresses under a
+// lane mask (rows of a share sit anywhere in the cache).
+__device__ __forceinline__ void dma16_vm(uint64_t vaddr, uint32_t lds_wave_base, uint64_t lanes) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)lanes);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(lanes >> 32));
+  uint64_t save;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_and_b32 exec_lo, exec_lo, %3\n\t"
+      "s_and_b32 exec_hi, exec_hi, %4\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b64 exec, %0\n\t"
+      "s_nop 4"
+      : "=&s"(save)
+      : "v"(vaddr), "s"(m0), "s"(lo), "s"(hi)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t idx_slot_off(int t, int w) {
+  return IDX_OFF + (uint32_t)(t & (IDX_SLOTS - 1)) * (WAVES * 32) + (uint32_t)w * 32;
+}
+
+// Fetch the list entries of this wave's share of tile t (lanes 0..7; none
+// when !live or past top-k): exactly one instruction.
+__device__ __forceinline__ void issue_sparse_index(const Params& p, uint8_t* smem, int b, int t, bool live) {
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int j0 = live ? t * TILE + 8 * w : 0;
+  const int32_t* lst = p.block_tables + (size_t)b * p.bt_stride + j0;
+  const uint64_t lanes = __builtin_amdgcn_ballot_w64(live && lane < 8 && j0 + lane < p.sparse_k);
+  dma4_m(lst, (uint32_t)lane * 4, lds_addr(smem) + idx_slot_off(t, w), lanes);
+}
+
+// The DMA of this wave's share of tile t into buffer buf (its entries have
+// landed): tile_loads<FP8>() instructions, empty rows zero-filled.
+template <bool FP8>
+__device__ __forceinline__ void issue_sparse_share(const Params& p, uint8_t* smem, uint32_t buf, int t) {
+  // (the empty asm makes the lane id opaque, so the per-lane offsets below are
+  // recomputed at each call instead of being hoisted into registers that would
+  // stay live across the whole tile loop)
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int w = uniform(threadIdx.x >> 6);
+  const int j0 = t * TILE + 8 * w;
+  const uint32_t lds0 = lds_addr(smem);
+  auto pick = [&](int r) {  // entry r of the share (lane-varying r), read from the ring
+    const int v = *(const __attribute__((address_space(3))) int*)((const __attribute__((address_space(3))) uint8_t*)smem +
+                                                                 idx_slot_off(t, w) + 4 * r);
+    return (j0 + r < p.sparse_k) ? v : -1;  // positions past top-k hold stale ring data
+  };
+  const int mine = pick(lane & 7);  // lane i < 8: entry i
+  const uint32_t live8 = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && mine >= 0) & 0xFFu;
+  if (lane == 0)
+    *((__attribute__((address_space(3))) uint8_t*)smem + VMASK_OFF + (t & (IDX_SLOTS - 1)) * 4 + w) = (uint8_t)live8;
+  const uint64_t kv = (uint64_t)(uintptr_t)p.kv;
+  if (!FP8) {
+    const uint32_t lat = buf + 8 * w * 1024;
+    const uint32_t rope = buf + ROPE_OFF_BF16 + 8 * w * 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ei = uniform(__builtin_amdgcn_readlane(mine, i));
+      if (ei < 0) lds_zero16(smem, lat + i * 1024 + lane * 16);
+      const uint64_t a = kv + (uint64_t)max(ei, 0) * ROWB_BF16 + (uint32_t)((lane ^ swz_lat_bf16(8 * w + i)) << 4);
+      dma16_vm(a, lds0 + lat + i * 1024, ei >= 0 ? ~0ull : 0ull);
+    }
+    const int rr = lane >> 3;  // RoPE: 8 lanes per row
+    const int er = pick(rr);
+    if (er < 0) lds_zero16(smem, rope + lane * 16);
+    const uint64_t a = kv + (uint64_t)max(er, 0) * ROWB_BF16 + 1024 +
+                       (uint32_t)((((lane & 7) ^ swz_rope_bf16(8 * w + rr))) << 4);
+    dma16_vm(a, lds0 + rope, __builtin_amdgcn_ballot_w64(er >= 0));
+  } else {
+    const uint32_t lat = buf + 8 * w * 512;
+    const uint32_t rope = buf + ROPE_OFF_FP8 + 8 * w * 64;
+    const int hi = lane >> 5;  // latent: rows 2k (lanes 0..31) and 2k + 1 (lanes 32..63)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 2 * k + hi;
+      const int er = pick(r);
+      if (er < 0) lds_zero16(smem, lat + k * 1024 + lane * 16);
+      const uint64_t a = kv + (uint64_t)max(er, 0) * ROWB_FP8 + (uint32_t)(((lane & 31) ^ swz_lat_fp8(8 * w + r)) << 4);
+      dma16_vm(a, lds0 + lat + k * 1024, __builtin_amdgcn_ballot_w64(er >= 0));
+    }
+    const int rr = (lane & 31) >> 2;  // RoPE: 4 lanes per row, lanes 0..31
+    const int er = pick(rr);
+    if (lane < 32 && er < 0) lds_zero16(smem, rope + lane * 16);
+    const uint64_t a = kv + (uint64_t)max(er, 0) * ROWB_FP8 + 512 + (uint32_t)(((lane & 3) ^ swz_rope_fp8(8 * w + rr)) << 4);
+    dma16_vm(a, lds0 + rope, __builtin_amdgcn_ballot_w64(lane < 32 && er >= 0));
+  }
 }
 
 // ---------------------------------------------------------------- one segment
@@ -679,11 +835,15 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
 
   // Tile t has landed once at most the DMA ops of the n tiles issued after it
   // remain; a partial tile among them makes the count unknown, so drain.
+  // (Sparse layout: each tile's DMA is followed by the list fetch of the tile
+  // two further on, so the same wait also lands the entries the next share
+  // issue reads.)
+  constexpr int PER_TILE = LOADS + (PS == 0 ? 1 : 0);
   auto wait_tile = [&](int t, int n) {
     n = min(n, t1 - 1 - t);
     if (n <= 0 || (t + n + 1) * TILE > L) wait_vmcnt<0>();
-    else if (n == 1) wait_vmcnt<LOADS>();
-    else wait_vmcnt<2 * LOADS>();
+    else if (n == 1) wait_vmcnt<PER_TILE>();
+    else wait_vmcnt<2 * PER_TILE>();
   };
 
   const float c = p.scale_log2;
@@ -733,12 +893,16 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     }
   };
   // Masked path: causal edge tiles, and the first tile (which sets the reference).
-  auto masked_softmax = [&](f32x16 s, int t) {
-    const int tok0 = t * TILE + 8 * h;
+  auto masked_softmax = [&](f32x16 s, int t, uint32_t live) {
     float mx = -INFINITY;
+    // this lane half's tokens start at 8h: shift once, so that each bit test
+    // below has a constant position (no per-lane masks held in registers)
+    const uint32_t live_h = live >> (8 * h);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float v = (tok0 + 16 * (k >> 3) + (k & 7)) < n_vis ? s[k] * c : -INFINITY;
+      const int tk = 8 * h + 16 * (k >> 3) + (k & 7);  // token within the tile
+      const bool vis = (t * TILE + tk) < n_vis && ((live_h >> (16 * (k >> 3) + (k & 7))) & 1u);
+      const float v = vis ? s[k] * c : -INFINITY;
       s[k] = v;
       mx = fmaxf(mx, v);
     }
@@ -769,7 +933,16 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   for (int t = t0; t < t1; ++t) {
     const f32x16 s = s_next;
     TileLoad tl = no_load;
-    const bool fast = c_pos && st.ref_ready && (t + 1) * TILE <= min_vis;
+    // live rows of tile t (sparse layout: the shares' published bits; the
+    // dense layouts mask by position only)
+    uint32_t live = ~0u;
+    if constexpr (PS == 0) {
+      const __attribute__((address_space(3))) uint32_t* vm =
+          (const __attribute__((address_space(3))) uint32_t*)((__attribute__((address_space(3))) uint8_t*)smem +
+                                                               VMASK_OFF + (t & (IDX_SLOTS - 1)) * 4);
+      live = uniform(*vm);
+    }
+    const bool fast = c_pos && st.ref_ready && (t + 1) * TILE <= min_vis && live == ~0u;
     if (t + 1 < t1) {
       wait_tile(t + 1, 1);
       wait_lgkm0();
@@ -777,11 +950,19 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       // Tile t+3 goes to the buffer of tile t-1.  Even waves issue their share
       // now, odd waves at the P exchange below: two bursts of loads queue in the
       // CU's address unit instead of one burst from all four waves.
-      if (t + 3 < t1) {
-        tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
-        if ((w & 1) == 0 || !ACTIVE) {
-          issue_tile_share<FP8>(tl);
-          tl = no_load;
+      if constexpr (PS == 0) {
+        // sparse: every wave now, its share of tile t+3 then the entries of t+5
+        if (t + 3 < t1) {
+          issue_sparse_share<FP8>(p, smem, buf_of(t + 3), t + 3);
+          issue_sparse_index(p, smem, b, t + 5, t + 5 < t1);
+        }
+      } else {
+        if (t + 3 < t1) {
+          tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
+          if ((w & 1) == 0 || !ACTIVE) {
+            issue_tile_share<FP8>(tl);
+            tl = no_load;
+          }
         }
       }
       if (ACTIVE) {
@@ -796,7 +977,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
           for (int k = 0; k < QK_STEPS; ++k) fast_piece(s, nm, k);
           s_next = qk(buf_of(t + 1), no_fill);
         } else {
-          masked_softmax(s, t);
+          masked_softmax(s, t, live);
           s_next = qk(buf_of(t + 1), no_fill);
         }
       }
@@ -806,7 +987,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
 #pragma unroll
         for (int k = 0; k < QK_STEPS; ++k) fast_piece(s, nm, k);
       } else {
-        masked_softmax(s, t);
+        masked_softmax(s, t, live);
       }
     }
     if (!ACTIVE) {
@@ -885,11 +1066,24 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
 
   // page ids of the segment, then the first three tiles in flight before the
   // query loads
-  PageWin pw;
-  load_page_window<page_window<FP8>()>(p, b, ceil_div(L, PS), uniform((t0 * TILE) / PS), pw);
-  issue_tile<FP8, PS>(p, smem, 0, b, L, t0, pw);
-  if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1, pw);
-  if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2, pw);
+  PageWin pw{0, 0, 0};
+  if constexpr (PS == 0) {
+    // sparse: the list entries of the first four tiles (one ring slot each),
+    // then (landed) the first three tiles' rows, then the entries of the
+    // fifth, into the slot the first has just been read from
+#pragma unroll
+    for (int k = 0; k < IDX_SLOTS; ++k) issue_sparse_index(p, smem, b, t0 + k, t0 + k < t1);
+    wait_vmcnt<0>();
+    issue_sparse_share<FP8>(p, smem, 0, t0);
+    if (t0 + 1 < t1) issue_sparse_share<FP8>(p, smem, TILEB, t0 + 1);
+    if (t0 + 2 < t1) issue_sparse_share<FP8>(p, smem, 2 * TILEB, t0 + 2);
+    issue_sparse_index(p, smem, b, t0 + 4, t0 + 4 < t1);
+  } else {
+    load_page_window<page_window<FP8>()>(p, b, ceil_div(L, PS), uniform((t0 * TILE) / PS), pw);
+    issue_tile<FP8, PS>(p, smem, 0, b, L, t0, pw);
+    if (t0 + 1 < t1) issue_tile<FP8, PS>(p, smem, TILEB, b, L, t0 + 1, pw);
+    if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2, pw);
+  }
 
   // Query fragments (B operand): lane holds pair `col`; step kk < 32 covers latent
   // dims 16kk + 8h .. +8, steps 32..35 RoPE dims 512 + 16(kk-32) + 8h.
@@ -1053,7 +1247,7 @@ void mla_decode_kernel(Params p) {
   __syncthreads();  // the LDS plan is dead from here on
   while (x < end) {
     // walk the cost space forward from request b
-    const int L = uniform(p.seq_lens[b]);
+    const int L = uniform(req_len(p, b));
     int r0;
     const int qb = uniform(request_rows(p, b, r0));
     const int T = uniform(request_tiles(p, b));
@@ -1121,58 +1315,83 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int head = item - row * H;
   int b;
   if (p.qo_indptr != nullptr) {
-    int lo = 0, hi = p.batch;  // qo_indptr[lo] <= row < qo_indptr[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.qo_indptr[mid] <= row) lo = mid; else hi = mid;
+    // the row's request, lane-parallel in one round trip: qo_indptr starts at
+    // 0 and increases strictly, so b + 1 entries of [0, B) are <= row
+    int cnt = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += 128) {
+      const int j0 = c0 + lane, j1 = c0 + 64 + lane;
+      const bool in0 = j0 < p.batch && p.qo_indptr[j0] <= row;
+      const bool in1 = j1 < p.batch && p.qo_indptr[j1] <= row;
+      cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(in0)) +
+             __builtin_popcountll(__builtin_amdgcn_ballot_w64(in1));
     }
-    b = lo;
+    b = uniform(cnt - 1);
   } else {
     b = row / p.q_len_fixed;
   }
-  int r0;
-  request_rows(p, b, r0);
+  // everything the segment addresses depend on, in one round trip
+  const int r0 = p.qo_indptr != nullptr ? p.qo_indptr[b] : b * p.q_len_fixed;
+  const int C = p.ws_plan[0];
+  const int L = req_len(p, b);
+  const int tile_off = p.ws_plan[2 + b];
+  const int unit_off = p.ws_plan[3 + p.batch + b];
   const int pair = (row - r0) * H + head;
   const int pb = pair / PAIRS_BLOCK;
   const int pl = pair - pb * PAIRS_BLOCK;
-  const int C = p.ws_plan[0];
-  const int T = max(0, ceil_div(p.seq_lens[b], TILE));
-  const int u = p.ws_plan[3 + p.batch + b] + pb;
-  const int U0 = p.ws_plan[2 + b] + pb * T + (u + 1) * p.seg_cost;  // cost position of the unit's first tile
+  const int T = max(0, ceil_div(L, TILE));
+  const int u = unit_off + pb;
+  const int U0 = tile_off + pb * T + (u + 1) * p.seg_cost;  // cost position of the unit's first tile
   const int g0 = U0 / C;
   const int g1 = (U0 + T - 1) / C;
   const int nseg = (T > 0) ? g1 - g0 + 1 : 0;  // a request with no rows (a sequence shard may have none) has no segment
   const float* mlb = p.ws_ml + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * 2;  // segment s at + s * PAIRS_BLOCK * 2
   const uint16_t* ob = p.ws_o + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * D_V + 8 * lane;
-  // (max, sum) of up to 64 segments at a time, one per lane, all loads in flight together
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < nseg; c0 += 64) {
-    if (c0 + lane < nseg) M = fmaxf(M, mlb[(size_t)(c0 + lane) * PAIRS_BLOCK * 2]);
-  }
-  M = wave_max(M);
+  // One round trip before any arithmetic: the O rows of the first MB segments
+  // and the (max, sum) of the first 64 (one per lane) are all in flight
+  // together; lane l holds dims 8l .. 8l + 8 of each O row.
+  constexpr int MB = 16;  // O rows in flight
   // a sink is one more softmax term with no value row: it joins the max and
   // the denominator
   const float sink = (p.sinks != nullptr) ? p.sinks[head] * LOG2E : -INFINITY;
+  const size_t o_step = (size_t)PAIRS_BLOCK * D_V;
+  const size_t ml_step = (size_t)PAIRS_BLOCK * 2;
+  u32x4 o[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+    if (i < nseg) o[i] = *(const u32x4*)(ob + (size_t)i * o_step);
+  float m_first = -INFINITY, s_first = 0.f;
+  if (lane < nseg) {
+    m_first = mlb[(size_t)lane * ml_step];
+    s_first = mlb[(size_t)lane * ml_step + 1];
+  }
+  float M = m_first;
+  for (int c0 = 64; c0 < nseg; c0 += 64) {
+    if (c0 + lane < nseg) M = fmaxf(M, mlb[(size_t)(c0 + lane) * ml_step]);
+  }
+  M = wave_max(M);
   M = fmaxf(M, sink);
   float den = 0.f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int c0 = 0; c0 < nseg; c0 += 64) {
     float wl = 0.f;  // this lane's segment weight 2^(m - M)
     if (c0 + lane < nseg) {
-      const float* ml = mlb + (size_t)(c0 + lane) * PAIRS_BLOCK * 2;
-      const float m = ml[0];
+      float m = m_first, sv = s_first;
+      if (c0 > 0) {
+        m = mlb[(size_t)(c0 + lane) * ml_step];
+        sv = mlb[(size_t)(c0 + lane) * ml_step + 1];
+      }
       wl = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      den += wl * ml[1];
+      den += wl * sv;
     }
-    // O of eight segments in flight at a time; lane holds dims 8 lane .. 8 lane + 8
     const int cn = min(64, nseg - c0);
-    for (int s0 = 0; s0 < cn; s0 += 8) {
-      u32x4 o[8];
+    for (int s0 = 0; s0 < cn; s0 += MB) {
+      if (c0 + s0 > 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (s0 + i < cn) o[i] = *(const u32x4*)(ob + (size_t)(c0 + s0 + i) * PAIRS_BLOCK * D_V);
+        for (int i = 0; i < MB; ++i)
+          if (s0 + i < cn) o[i] = *(const u32x4*)(ob + (size_t)(c0 + s0 + i) * o_step);
+      }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < MB; ++i) {
         if (s0 + i < cn) {
           const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), s0 + i));
 #pragma unroll
@@ -1305,13 +1524,20 @@ WsLayout workspace_layout(int grid, int64_t units) {
   return l;
 }
 
-int validate(const mla_decode_dims_t* d, int32_t max_seq_len, int32_t max_q_len, bool packed) {
-  if (d == nullptr) return MLA_ERR_NULL_POINTER;
-  if (d->batch < 1 || d->batch > MLA_MAX_BATCH || max_seq_len < 1 || d->num_pages < 1) return MLA_ERR_BAD_SHAPE;
+// Checks shared by the paged and the sparse layouts.
+int validate_common(const mla_decode_dims_t* d) {
   if (d->num_heads <= 0 || d->num_heads % 16 != 0) return MLA_ERR_BAD_HEADS;
   if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64) return MLA_ERR_BAD_PAGE_SIZE;
   if (d->kv_lora_rank != 512 || d->qk_rope_head_dim != 64) return MLA_ERR_BAD_HEAD_DIMS;
   if (d->kv_dtype != MLA_KV_BF16 && d->kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_BAD_DTYPE;
+  return MLA_OK;
+}
+
+int validate(const mla_decode_dims_t* d, int32_t max_seq_len, int32_t max_q_len, bool packed) {
+  if (d == nullptr) return MLA_ERR_NULL_POINTER;
+  if (d->batch < 1 || d->batch > MLA_MAX_BATCH || max_seq_len < 1 || d->num_pages < 1) return MLA_ERR_BAD_SHAPE;
+  const int c = validate_common(d);
+  if (c != MLA_OK) return c;
   if (max_q_len < 1 || d->total_q < 1) return MLA_ERR_BAD_Q_LEN;
   if (!packed && (d->q_len_fixed != max_q_len || (int64_t)d->batch * d->q_len_fixed != d->total_q))
     return MLA_ERR_BAD_Q_LEN;
@@ -1320,6 +1546,22 @@ int validate(const mla_decode_dims_t* d, int32_t max_seq_len, int32_t max_q_len,
   // 32-bit cost arithmetic on device
   if (max_units(d, max_q_len) * ((max_seq_len + TILE - 1) / TILE + SEG_COST_MAX) >= (int64_t)1 << 30)
     return MLA_ERR_BAD_SHAPE;
+  return MLA_OK;
+}
+
+// Sparse top-k layout: every query row is a unit group of its own.
+int64_t sparse_units(const mla_decode_dims_t* d) {
+  return (int64_t)d->total_q * ((d->num_heads + PAIRS_BLOCK - 1) / PAIRS_BLOCK);
+}
+
+int validate_sparse(const mla_decode_dims_t* d, int32_t top_k) {
+  if (d == nullptr) return MLA_ERR_NULL_POINTER;
+  const int c = validate_common(d);
+  if (c != MLA_OK) return c;
+  if (d->total_q < 1 || d->total_q > MLA_MAX_BATCH || d->num_pages < 1 || top_k < 1 || top_k > MLA_MAX_TOP_K)
+    return MLA_ERR_BAD_SHAPE;
+  if (d->block_table_stride < top_k) return MLA_ERR_BAD_BLOCK_TABLE;
+  if (sparse_units(d) * ((top_k + TILE - 1) / TILE + SEG_COST_MAX) >= (int64_t)1 << 30) return MLA_ERR_BAD_SHAPE;
   return MLA_OK;
 }
 
@@ -1361,6 +1603,16 @@ size_t mla_decode_paged_workspace_size(const mla_decode_dims_t* dims, int32_t ma
   return workspace_layout(grid, max_units(dims, max_q_len)).total;
 }
 
+size_t mla_decode_paged_ex_workspace_size(const mla_decode_dims_t* dims, int32_t max_seq_len, int32_t max_q_len,
+                                          int want_lse, const mla_decode_options_t* opts) {
+  const int32_t top_k = opts != nullptr ? opts->sparse_top_k : 0;
+  if (top_k <= 0) return mla_decode_paged_workspace_size(dims, max_seq_len, max_q_len, want_lse);
+  if (dims == nullptr || validate_sparse(dims, top_k) != MLA_OK) return 0;
+  int grid = 0;
+  if (device_grid(&grid) != MLA_OK) return 0;
+  return workspace_layout(grid, sparse_units(dims)).total;
+}
+
 int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_tables, const int32_t* seq_lens,
                      const int32_t* qo_indptr, int32_t max_seq_len, int32_t max_q_len, float bmm1_scale,
                      float bmm2_scale, int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
@@ -1373,21 +1625,25 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
                         const int32_t* qo_indptr, int32_t max_seq_len, int32_t max_q_len, float bmm1_scale,
                         float bmm2_scale, int causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
                         const mla_decode_dims_t* dims, void* stream, const mla_decode_options_t* opts) {
-  if (!q || !kv_cache || !block_tables || !seq_lens || !out || !workspace || !dims) return MLA_ERR_NULL_POINTER;
+  const int32_t top_k = opts != nullptr ? opts->sparse_top_k : 0;
+  const bool sparse = top_k > 0;
+  if (!q || !kv_cache || !block_tables || (!seq_lens && !sparse) || !out || !workspace || !dims)
+    return MLA_ERR_NULL_POINTER;
   if (opts != nullptr && (((uintptr_t)opts->bmm1_scale | (uintptr_t)opts->bmm2_scale | (uintptr_t)opts->sinks |
                             (uintptr_t)opts->seq_lens_global) & 3))
     return MLA_ERR_MISALIGNED;
   const bool dcp = opts != nullptr && opts->seq_lens_global != nullptr;
   if (dcp && (opts->cp_world < 1 || opts->cp_rank < 0 || opts->cp_rank >= opts->cp_world)) return MLA_ERR_BAD_SHAPE;
   if (dcp && lse == nullptr) return MLA_ERR_NULL_POINTER;
-  const int v = validate(dims, max_seq_len, max_q_len, qo_indptr != nullptr);
+  if (top_k < 0 || (sparse && dcp)) return MLA_ERR_BAD_SHAPE;
+  const int v = sparse ? validate_sparse(dims, top_k) : validate(dims, max_seq_len, max_q_len, qo_indptr != nullptr);
   if (v != MLA_OK) return v;
   if (((uintptr_t)q | (uintptr_t)kv_cache | (uintptr_t)out | (uintptr_t)workspace) & 15) return MLA_ERR_MISALIGNED;
   if (lse != nullptr && ((uintptr_t)lse & 3)) return MLA_ERR_MISALIGNED;
   int grid = 0;
   const int gs = device_grid(&grid);
   if (gs != MLA_OK) return gs;
-  const WsLayout wl = workspace_layout(grid, max_units(dims, max_q_len));
+  const WsLayout wl = workspace_layout(grid, sparse ? sparse_units(dims) : max_units(dims, max_q_len));
   if (workspace_bytes < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
   Params p;
@@ -1420,13 +1676,25 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   p.seq_lens_global = dcp ? opts->seq_lens_global : nullptr;
   p.cp_world = dcp ? opts->cp_world : 1;
   p.cp_rank = dcp ? opts->cp_rank : 0;
+  p.sparse_k = 0;
+  if (sparse) {
+    // each query row is a request of its own whose rows are its list entries
+    p.batch = dims->total_q;
+    p.q_len_fixed = 1;
+    p.qo_indptr = nullptr;
+    p.seq_lens = nullptr;
+    p.causal = 0;
+    p.sparse_k = top_k;
+  }
 
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = dims->kv_dtype == MLA_KV_FP8_E4M3FN;
   void* ev0 = g_ev_start.load(std::memory_order_relaxed);
   void* ev1 = g_ev_stop.load(std::memory_order_relaxed);
   if (ev0 != nullptr) (void)hipEventRecord((hipEvent_t)ev0, s);
-  switch (dims->page_size) {
+  if (sparse) {
+    fp8 ? launch_decode<true, 0>(p, s) : launch_decode<false, 0>(p, s);
+  } else switch (dims->page_size) {
     case 16: fp8 ? launch_decode<true, 16>(p, s) : launch_decode<false, 16>(p, s); break;
     case 32: fp8 ? launch_decode<true, 32>(p, s) : launch_decode<false, 32>(p, s); break;
     default: fp8 ? launch_decode<true, 64>(p, s) : launch_decode<false, 64>(p, s); break;

@@ -224,6 +224,40 @@ def named_workload(name, poison=True, **overrides):
     return make_workload(name, poison=poison, **spec)
 
 
+def sparse_lists(w, top_k, seed, *, empty_frac=0.0, repeat_frac=0.0, empty_rows=()):
+    """Seeded top-k lists for a workload's query rows: int32 [total_q, top_k]
+    of flat cache-row ids (page * page_size + slot).
+
+    Row r draws min(top_k, L_b) distinct positions of its request b uniformly
+    (the selection an indexer would hand over; no trained indexer here), in
+    random order, then fills the rest of the row with -1.  empty_frac of the
+    listed entries are then overwritten with -1 and repeat_frac with a copy of
+    another listed entry; rows in empty_rows are all -1.  Draw order: per row,
+    the positions, then the empties, then the repeats.
+    """
+    rng = np.random.default_rng(seed)
+    ps = w.page_size
+    out = np.full((w.total_q, top_k), -1, dtype=np.int32)
+    q_lens = w.q_lens()
+    r = 0
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        for _ in range(int(q_lens[b])):
+            n = min(top_k, L)
+            pos = rng.choice(L, size=n, replace=False)
+            ids = w.block_tables[b, pos // ps].astype(np.int64) * ps + pos % ps
+            out[r, :n] = ids
+            if empty_frac > 0:
+                out[r, np.flatnonzero(rng.random(n) < empty_frac)] = -1
+            if repeat_frac > 0 and n > 1:
+                dst = np.flatnonzero(rng.random(n) < repeat_frac)
+                out[r, dst] = out[r, rng.integers(0, n, size=dst.size)]
+            if r in empty_rows:
+                out[r] = -1
+            r += 1
+    return out
+
+
 def to_device_tensors(w, device="cuda"):
     """torch tensors for the binding: q bf16, kv bf16/fp8, int32 metadata."""
     import torch

@@ -90,9 +90,10 @@ MISALIGNED = 6
 
 
 def test_options_struct_and_misaligned_option_pointers():
-    # three pointers, in header order
-    assert ctypes.sizeof(binding.MlaOptions) == 40
+    # four pointers then three int32, in header order (padded to 48)
+    assert ctypes.sizeof(binding.MlaOptions) == 48
     assert binding.MlaOptions.sinks.offset == 16
+    assert binding.MlaOptions.sparse_top_k.offset == 40
     for field in ("bmm1_scale", "bmm2_scale", "sinks"):
         opts = binding.MlaOptions(None, None, None)
         setattr(opts, field, FAKE + 2)
@@ -122,3 +123,30 @@ def test_dcp_options_and_merge_partials_reject_bad_arguments():
     assert lib.mla_merge_partials(FAKE, FAKE, 2, 0, FAKE, None, None) == BAD_SHAPE
     assert lib.mla_merge_partials(FAKE + 8, FAKE, 2, 16, FAKE, None, None) == MISALIGNED
     assert lib.mla_merge_partials(FAKE, FAKE + 2, 2, 16, FAKE, None, None) == MISALIGNED
+
+
+NO_DEVICE = 12
+
+
+def test_sparse_options_reject_bad_arguments():
+    """The sparse top-k layout: shape checks come before any device query; a
+    call that passes them (seq_lens may be NULL) reaches the device lookup."""
+    BAD_SHAPE, BAD_BLOCK_TABLE, NULL = 10, 9, 1
+
+    def ex(dims, k, sl=None, opts_over=None, lse=FAKE):
+        opts = binding.MlaOptions(None, None, None, None, 1, 0, k)
+        for f, v in (opts_over or {}).items():
+            setattr(opts, f, v)
+        return binding.mla_decode_paged_ex(FAKE, FAKE, FAKE, sl, None, 1, 1, 1.0, 1.0, False, FAKE, lse, FAKE,
+                                           1 << 30, dims, opts, stream=0)
+    sd = lambda **o: _dims(**{**dict(batch=3, q_len_fixed=1, total_q=3, block_table_stride=64), **o})
+    assert ex(sd(), -1, sl=FAKE) == BAD_SHAPE                                   # negative top-k
+    assert ex(sd(), 65) == BAD_BLOCK_TABLE                                      # list wider than its row
+    assert ex(sd(total_q=1025, batch=1025), 64) == BAD_SHAPE                    # too many query rows
+    assert ex(sd(block_table_stride=(1 << 20) + 1), (1 << 20) + 1) == BAD_SHAPE  # top-k above the limit
+    assert ex(sd(num_heads=24), 64) == 2                                        # shared shape checks still apply
+    assert ex(sd(), 64, opts_over=dict(seq_lens_global=FAKE, cp_world=2)) == BAD_SHAPE  # not with DCP
+    assert ex(sd(), 64) == NO_DEVICE                                            # NULL seq_lens is fine here
+    assert ex(sd(), 0) == NULL                                                  # ... but not in the paged layout
+    opts = binding.MlaOptions(None, None, None, None, 1, 0, 65)
+    assert binding.mla_decode_paged_ex_workspace_size(sd(), 1, 1, False, opts) == 0

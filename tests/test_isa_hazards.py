@@ -42,7 +42,7 @@ def library_asm(tmp_path_factory):
 @pytest.fixture(scope="module")
 def decode_bodies(library_asm):
     bodies = {n: b for n, b in ih.kernel_bodies(library_asm) if "mla_decode_kernel" in n}
-    assert len(bodies) == 6, sorted(bodies)  # {bf16, fp8} x page size {16, 32, 64}
+    assert len(bodies) == 8, sorted(bodies)  # {bf16, fp8} x (page size {16, 32, 64} + the sparse layout)
     return bodies
 
 
@@ -119,7 +119,8 @@ def test_checker_accepts_compiler_scheduled_mfma(tmp_path):
 
 
 def test_checker_finds_planted_hazards(decode_bodies):
-    body = next(iter(decode_bodies.values()))
+    # the fp8, page-size-16 kernel (whose fences guard reads the checker must see)
+    body = next(b for n, b in decode_bodies.items() if "ILb1ELi16E" in n)
     assert not ih.check_body(body)
     # a read of an MFMA result right after the MFMA
     i = next(k for k, l in enumerate(body) if "v_mfma" in l)
