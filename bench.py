@@ -12,6 +12,9 @@ the same workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
                   [--no-cpu-baseline] [--all]
+
+NAME is one of the paged workloads (paged_mla_decode_03_amd.inputs.WORKLOADS)
+or the sparse top-k workload sparse_topk_decode (SPARSE_WORKLOADS).
 """
 
 import argparse
@@ -95,12 +98,146 @@ def profiled_traffic(workload):
     return None
 
 
-def run_workload(name, steps, warmup, want_cpu, rotate=3):
+def time_steps(step, steps, warmup):
+    """Run warmup untimed steps, then time exactly `steps` steps (bracketed by
+    device synchronisation) with the library's decode-kernel events recorded
+    on the launch stream.  Returns (ms per step, mean decode-kernel ms)."""
     import numpy as np
     import torch
     from paged_mla_decode_03_amd import binding
+    log(f"[bench] warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        binding.set_kernel_events(ev[i][0], ev[i][1])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    binding.set_kernel_events(None, None)
+    return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def roofline(counts, kern_ms, name):
+    """The decode kernel against its bound: HBM if its algorithmic bytes take
+    longer at peak than its algorithmic flops at the bf16 MFMA peak."""
+    from paged_mla_decode_03_amd.metrics import PEAK_HBM_GBS, PEAK_MFMA_TFLOPS
+    t_hbm = counts["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_mfma = counts["flops"] / (PEAK_MFMA_TFLOPS["bf16"] * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = counts["bytes"] / (kern_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(name)}
+    achieved = counts["flops"] / (kern_ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
+            "frac": achieved / PEAK_MFMA_TFLOPS["bf16"], "traffic": profiled_traffic(name)}
+
+
+def sparse_cpu_baseline(w, lists, budget_s=10.0):
+    """The sparse oracle as it stands on whole query rows (cycling), about
+    budget_s seconds of CPU work."""
+    import numpy as np
+    from oracle.sparse import reference_sparse_decode
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    R = lists.shape[0]
+    calls, tokens = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        r = calls % R
+        reference_sparse_decode(w.q_bits[r:r + 1], w.kv_bits, w.kv_dtype, lists[r:r + 1], w.bmm1_scale,
+                                w.bmm2_scale)
+        calls += 1
+        tokens += int((lists[r] >= 0).sum())
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "KV-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{calls} whole query rows of {w.name} (cycling through its {R}), {tokens} listed rows "
+                      f"in {dt:.1f} s, float64 NumPy"}
+
+
+def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
+    """One step = one sparse top-k decode call over the whole batch."""
+    import torch
+    from paged_mla_decode_03_amd import binding
+    from paged_mla_decode_03_amd.inputs import named_sparse_workload, SPARSE_WORKLOADS
+    from paged_mla_decode_03_amd.metrics import sparse_counts
+
+    log(f"[bench] generating workload {name}")
+    w, lists = named_sparse_workload(name, poison=False)
+    spec = SPARSE_WORKLOADS[name]
+    K = int(spec["top_k"])
+    counts = sparse_counts(lists, K, w.num_heads, 2 if w.kv_dtype == "bf16" else 1, w.want_lse)
+    kv = torch.from_numpy(w.kv_bits)
+    kv = (kv.view(torch.bfloat16) if w.kv_dtype == "bf16" else kv.view(torch.float8_e4m3fn)).cuda()
+    q = torch.from_numpy(w.q_bits).view(torch.bfloat16).cuda()
+    idx = torch.from_numpy(lists).cuda()
+    nbytes = binding.sparse_workspace_bytes_for(q, kv, idx, top_k=K, return_lse=w.want_lse)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(tuple(q.shape[:-1]) + (512,), dtype=torch.bfloat16, device="cuda")
+    binding.decode_sparse(q, kv, ws, idx, top_k=K, out=out, bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale)
+    dims, _, _ = binding._sparse_dims(q, kv, idx)
+    opts = binding.MlaOptions(None, None, None, None, 1, 0, K)
+    stream = torch.cuda.current_stream().cuda_stream
+    kvs = [kv] + [kv.clone() for _ in range(max(1, rotate) - 1)]
+    qs = [q] + [q.clone() for _ in range(max(1, rotate) - 1)]
+    n_step = [0]
+
+    def step():
+        i = n_step[0] % len(kvs)
+        rc = binding.mla_decode_paged_ex(qs[i].data_ptr(), kvs[i].data_ptr(), idx.data_ptr(), None, None, 1, 1,
+                                         w.bmm1_scale, w.bmm2_scale, False, out.data_ptr(), None, ws.data_ptr(),
+                                         nbytes, dims, opts, stream=stream)
+        n_step[0] += 1
+        if rc != 0:
+            raise RuntimeError(binding.mla_status_string(rc))
+
+    ms_step, kern_ms = time_steps(step, steps, warmup)
+    res = {
+        "metric": METRIC,
+        "value": counts["kv_tokens"] / (ms_step * 1e-3),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma",
+        "data": f"synthetic (seeded N(0,1) q/kv, shuffled pages, seeded top-k selections of each request; "
+                f"{max(1, rotate)} cache copies rotated across steps)",
+        "config": {"workload": name, "rows": w.total_q, "heads": w.num_heads, "top_k": K,
+                   "seq_lens": list(spec["seq_len_range"]), "page_size": w.page_size, "kv_dtype": w.kv_dtype,
+                   "lse": w.want_lse, "kv_tokens": counts["kv_tokens"]},
+        "tflops": counts["flops"] / (ms_step * 1e-3) / 1e12,
+        "gbps": counts["bytes"] / (ms_step * 1e-3) / 1e9,
+        "decode_kernel_ms": kern_ms,
+        "kernel_source_sha256": kernel_source_sha256(),
+        "roofline": roofline(counts, kern_ms, name),
+    }
+    if want_cpu:
+        log("[bench] cpu baseline (oracle)")
+        res["cpu_baseline"] = sparse_cpu_baseline(w, lists)
+    return res
+
+
+def run_workload(name, steps, warmup, want_cpu, rotate=3):
+    import torch
+    from paged_mla_decode_03_amd import binding
     from paged_mla_decode_03_amd.inputs import named_workload, to_device_tensors, WORKLOADS
-    from paged_mla_decode_03_amd.metrics import counts_for_workload, PEAK_HBM_GBS, PEAK_MFMA_TFLOPS
+    from paged_mla_decode_03_amd.metrics import counts_for_workload
 
     log(f"[bench] generating workload {name}")
     w = named_workload(name, poison=False)
@@ -138,41 +275,10 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
-    log(f"[bench] warmup {warmup}")
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # decode-kernel events, recorded by the library on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    log(f"[bench] timing {steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        binding.set_kernel_events(ev[i][0], ev[i][1])
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    binding.set_kernel_events(None, None)
-    ms_step = (t1 - t0) * 1e3 / steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
+    ms_step, kern_ms = time_steps(step, steps, warmup)
     kv_bytes_per = 2 if w.kv_dtype == "bf16" else 1
     dtype = "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma"
-    t_hbm = counts["bytes"] / (PEAK_HBM_GBS * 1e9)
-    t_mfma = counts["flops"] / (PEAK_MFMA_TFLOPS["bf16"] * 1e12)
-    if t_hbm >= t_mfma:
-        achieved = counts["bytes"] / (kern_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(name)}
-    else:
-        achieved = counts["flops"] / (kern_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": achieved / PEAK_MFMA_TFLOPS["bf16"], "traffic": profiled_traffic(name)}
+    roof = roofline(counts, kern_ms, name)
     spec = WORKLOADS[name]
     res = {
         "metric": METRIC,
@@ -229,14 +335,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    res = run_workload(args.workload, args.steps, args.warmup, not args.no_cpu_baseline, args.rotate)
+    from paged_mla_decode_03_amd.inputs import WORKLOAD_ORDER, SPARSE_WORKLOADS
+
+    def run(name, want_cpu):
+        fn = run_sparse_workload if name in SPARSE_WORKLOADS else run_workload
+        return fn(name, args.steps, args.warmup, want_cpu, args.rotate)
+
+    res = run(args.workload, not args.no_cpu_baseline)
     if args.all:
-        from paged_mla_decode_03_amd.inputs import WORKLOAD_ORDER
-        for name in WORKLOAD_ORDER:
+        for name in WORKLOAD_ORDER + list(SPARSE_WORKLOADS):
             if name == args.workload:
                 continue
-            r = run_workload(name, args.steps, args.warmup, False, args.rotate)
-            log("[bench-extra] " + json.dumps(r))
+            log("[bench-extra] " + json.dumps(run(name, False)))
     if args.copy_bytes > 0:
         n = (args.copy_bytes + 15) // 16 * 16
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

@@ -217,6 +217,25 @@ WORKLOADS = {
 
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Sparse top-k decode (the layout of mla_decode_options_t.sparse_top_k): a
+# DeepSeek-shaped batch whose every query row attends to a top-k selection of
+# its request.  The pages give no sparse configuration; this one takes the
+# decode shape above (128 heads, page size 64, bf16 cache) with top-k 2048
+# from requests longer than the list.
+SPARSE_WORKLOADS = {
+    "sparse_topk_decode": dict(seed=6, batch=64, seq_len_range=(4096, 16384), num_heads=128, q_len=1,
+                               page_size=64, bmm1_scale=INV_SQRT_192, bmm2_scale=1.0, causal=False,
+                               want_lse=False, top_k=2048, list_seed=7),
+}
+
+
+def named_sparse_workload(name, poison=True):
+    """(workload, int32 lists [total_q, top_k]) of a named sparse workload."""
+    spec = dict(SPARSE_WORKLOADS[name])
+    top_k, list_seed = spec.pop("top_k"), spec.pop("list_seed")
+    w = make_workload(name, poison=poison, **spec)
+    return w, sparse_lists(w, top_k, list_seed)
+
 
 def named_workload(name, poison=True, **overrides):
     spec = dict(WORKLOADS[name])

@@ -10,6 +10,12 @@ kernels split the work:
           KV rows query row i of request b sees (L_b - q_b + i + 1 when
           causal, L_b when dense); softmax work is not counted.
 KV-tokens = sum_b L_b (each cached row once per request).
+
+Sparse top-k layout: every query row r gathers its n_r live list entries, so
+  bytes = sum_r n_r*576*e_kv + R*H*576*2 + R*H*512*2 (+ R*H*4 lse)
+          + 4*R*K (the lists)
+  flops = 2*(576+512)*H * sum_r n_r
+  KV-tokens = sum_r n_r (a cache row once per query row that lists it).
 """
 
 import numpy as np
@@ -41,3 +47,12 @@ def workload_counts(seq_lens, q_lens, num_heads, page_size, kv_bytes, causal, wa
 def counts_for_workload(w):
     return workload_counts(w.seq_lens, w.q_lens(), w.num_heads, w.page_size, 2 if w.kv_dtype == "bf16" else 1,
                            w.causal, w.want_lse, w.qo_indptr is not None)
+
+
+def sparse_counts(lists, top_k, num_heads, kv_bytes, want_lse):
+    lists = np.asarray(lists)[:, :top_k]
+    R = int(lists.shape[0])
+    H = int(num_heads)
+    live = int((lists >= 0).sum())
+    nbytes = live * D_QK * kv_bytes + R * H * D_QK * 2 + R * H * D_V * 2 + (R * H * 4 if want_lse else 0) + 4 * R * top_k
+    return dict(kv_tokens=live, bytes=int(nbytes), flops=int(2 * (D_QK + D_V) * H * live), rows=R)
