@@ -58,6 +58,9 @@ class MlaProblem:
     sinks         float [H] or None: per-head sink logits (natural-log units, on
                   the scale of bmm1_scale * q.k), one more term of every softmax
                   denominator with no value row
+    q_dtype       "bf16" (q_bits uint16 codes) or "fp8_e4m3fn" (q_bits uint8
+                  codes: a query quantised to fp8 with its q_scale folded into
+                  bmm1_scale, FlashInfer PR #1248 / vLLM forward_mqa)
     """
 
     q_bits: np.ndarray
@@ -71,6 +74,7 @@ class MlaProblem:
     bmm2_scale: float
     causal: bool
     sinks: Optional[np.ndarray] = None
+    q_dtype: str = "bf16"
 
     @property
     def batch(self):
@@ -99,6 +103,14 @@ def _decode_kv(problem, bits):
     if problem.kv_dtype == "fp8_e4m3fn":
         return e4m3fn_bits_to_f64(bits)
     raise ValueError(f"unknown kv dtype {problem.kv_dtype!r}")
+
+
+def _decode_q(problem, bits):
+    if problem.q_dtype == "bf16":
+        return bf16_bits_to_f64(bits)
+    if problem.q_dtype == "fp8_e4m3fn":
+        return e4m3fn_bits_to_f64(bits)
+    raise ValueError(f"unknown query dtype {problem.q_dtype!r}")
 
 
 def visible_count(L, q_b, i, causal):
@@ -140,7 +152,7 @@ def _masked_logits(problem, b, Kb, lo=0, hi=None):
     H = problem.num_heads
     if hi is None:
         hi = L
-    Q = bf16_bits_to_f64(problem.q_bits[r_b:r_b + q_b]).reshape(q_b * H, D_QK)
+    Q = _decode_q(problem, problem.q_bits[r_b:r_b + q_b]).reshape(q_b * H, D_QK)
     S = (Q @ Kb.T) * float(problem.bmm1_scale)
     n = np.array([visible_count(L, q_b, i, problem.causal) for i in range(q_b)])
     n_rows = np.repeat(n, H)  # row index = i*H + h

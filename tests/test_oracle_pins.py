@@ -439,3 +439,29 @@ def test_mutants_are_caught(monkeypatch):
     def reversed_rows(problem, b):  # token order lost in the gather
         return real_gather(problem, b)[::-1]
     assert _pins_catch(monkeypatch, "gather_request_rows", reversed_rows) > 0
+
+
+# ---------------------------------------------------------------- fp8 query
+
+def test_fp8_query_is_the_same_decode_of_its_values():
+    """Every E4M3FN value is exactly a bf16 value, so a problem whose query is
+    given as fp8 codes equals the same problem with those values as bf16
+    codes (the pinned bf16-query definition), bitwise in float64."""
+    import dataclasses
+    from helpers import to_bf16_bits, to_e4m3_bits, e4m3_round
+    rng = np.random.default_rng(30)
+    H = 16
+    q, ks = random_dense(rng, 2, H, [2, 1], [60, 9], kv_dtype="fp8_e4m3fn")
+    q8 = e4m3_round(q * 3.0)  # spread over the fp8 range, subnormals included
+    q8[0, 0, :8] = [448.0, -448.0, 2.0 ** -9, -(2.0 ** -9), 0.0, 1.5, -0.1015625, 240.0]
+    prob = build_paged(q8, ks, 32, rng=rng, q_lens=[2, 1], packed=True, bmm1=0.01, bmm2=0.5, causal=True,
+                       kv_dtype="fp8_e4m3fn")
+    assert np.array_equal(oracle.bf16_bits_to_f64(prob.q_bits), q8)  # bf16 holds the fp8 values exactly
+    prob8 = dataclasses.replace(prob, q_bits=to_e4m3_bits(q8), q_dtype="fp8_e4m3fn")
+    o, l = oracle.reference_decode(prob)
+    o8, l8 = oracle.reference_decode(prob8)
+    np.testing.assert_array_equal(o8, o)
+    np.testing.assert_array_equal(l8, l)
+    # and the codes do reach the logits: a different query gives a different result
+    prob8b = dataclasses.replace(prob8, q_bits=to_e4m3_bits(q8 * 0.5))
+    assert not np.allclose(oracle.reference_decode(prob8b)[1], l)
