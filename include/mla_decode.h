@@ -171,6 +171,14 @@ int mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_t
  *             lse = -inf (lse = sinks[h] with a sink).  total_q <= MLA_MAX_BATCH,
  *             K <= MLA_MAX_TOP_K; not combinable with DCP mode.  The workspace
  *             size comes from mla_decode_paged_ex_workspace_size().
+ * q_fp8       0: q holds bf16.  Nonzero: q holds OCP E4M3FN codes (uint8,
+ *             same [rows, H, 576] layout), a query quantised to fp8 whose
+ *             q_scale the caller folds into bmm1_scale (FlashInfer PR #1248:
+ *             q_scale / k_scale enter through bmm1; vLLM forward_mqa
+ *             multiplies bmm1 by q_scale * k_scale); QK^T then runs on the
+ *             fp8 matrix cores with fp32 accumulation (P.V stays bf16).  Needs
+ *             the fp8 cache (MLA_ERR_BAD_DTYPE otherwise) and the paged layout
+ *             (MLA_ERR_BAD_SHAPE with sparse_top_k).
  * All pointers must be 4-byte aligned and stay valid until the enqueued work
  * completes; the library only reads them.
  */
@@ -182,6 +190,7 @@ typedef struct {
   int32_t cp_world;
   int32_t cp_rank;
   int32_t sparse_top_k;
+  int32_t q_fp8;
 } mla_decode_options_t;
 
 /*

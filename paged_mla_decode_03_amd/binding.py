@@ -37,6 +37,7 @@ class MlaOptions(ctypes.Structure):
         ("cp_world", ctypes.c_int32),
         ("cp_rank", ctypes.c_int32),
         ("sparse_top_k", ctypes.c_int32),
+        ("q_fp8", ctypes.c_int32),
     ]
 
 
@@ -240,6 +241,8 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
 
     bmm1_scale / bmm2_scale: a float, or a one-element float32 device tensor
     read by the kernels at run time (so a captured graph follows updates).
+    query may be float8_e4m3fn with a float8_e4m3fn cache (its q_scale folded
+    into bmm1_scale by the caller): QK^T then runs on the fp8 matrix cores.
     sinks: None or a float32 device tensor [H] of per-head sink logits.
     dcp: None, or (seq_lens_global int32 device [B], cp_world, cp_rank) for the
     sequence-sharded partial mode (kv_cache / block_tables / seq_lens then hold
@@ -251,8 +254,11 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if query.dtype != torch.bfloat16:
-        raise TypeError("query must be bfloat16")
+    if query.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise TypeError("query must be bfloat16 (or float8_e4m3fn with a float8_e4m3fn cache)")
+    q8 = query.dtype == torch.float8_e4m3fn
+    if q8 and kv_cache.dtype != torch.float8_e4m3fn:
+        raise TypeError("an fp8 query needs a float8_e4m3fn cache")
     if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_tables and seq_lens must be int32")
     if qo_indptr is not None and (qo_indptr.dtype != torch.int32 or not qo_indptr.is_cuda):
@@ -283,12 +289,12 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
             raise TypeError("dcp seq_lens_global must be an int32 device tensor shaped like seq_lens")
         if not return_lse:
             raise ValueError("the sequence-sharded mode needs return_lse=True")
-    if b1 is None and b2 is None and sinks is None and dcp is None:
+    if b1 is None and b2 is None and sinks is None and dcp is None and not q8:
         rc = mla_decode_paged(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q, bmm1_scale,
                               bmm2_scale, causal, out, lse, workspace_buffer, ws_bytes, dims)
     else:
         opts = MlaOptions(_ptr(b1), _ptr(b2), _ptr(sinks), None if dcp is None else _ptr(dcp[0]),
-                          1 if dcp is None else int(dcp[1]), 0 if dcp is None else int(dcp[2]), 0)
+                          1 if dcp is None else int(dcp[1]), 0 if dcp is None else int(dcp[2]), 0, int(q8))
         rc = mla_decode_paged_ex(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q,
                                  1.0 if b1 is not None else bmm1_scale, 1.0 if b2 is not None else bmm2_scale,
                                  causal, out, lse, workspace_buffer, ws_bytes, dims, opts)

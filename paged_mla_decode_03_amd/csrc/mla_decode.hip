@@ -40,6 +40,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <algorithm>
+#include <type_traits>
 #include <atomic>
 #include <mutex>
 
@@ -272,6 +273,21 @@ __device__ __forceinline__ f32x16 mfma_first_vgpr(const bf16x8& a, const bf16x8&
   return d;
 }
 __device__ __forceinline__ void mfma_fence(f32x16& v) { asm volatile("s_nop 7\n\ts_nop 3" : "+v"(v)); }
+
+// The fp8 query path's QK^T: v_mfma_f32_32x32x64_f8f6f4 with both operands
+// OCP E4M3 (format fields 0), fp32 accumulation, 16 passes.  Its result needs
+// 20 wait states before any other instruction reads it (what the compiler
+// emits for the builtin), hence mfma8_fence().
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void mfma8_acc_vgpr(f32x16& acc, const i32x8& a, const i32x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ f32x16 mfma8_first_vgpr(const i32x8& a, const i32x8& b) {
+  f32x16 d;
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma8_fence(f32x16& v) { asm volatile("s_nop 15\n\ts_nop 3" : "+v"(v)); }
 
 // ---------------------------------------------------------------- tile layout
 //
@@ -717,9 +733,9 @@ struct SegState {
   bool ref_ready;  // wave-uniform: every lane's m_ref is set
 };
 
-template <bool FP8, int PS, bool ACTIVE>
+template <bool FP8, int PS, bool ACTIVE, bool Q8, typename QF>
 __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int b, int L, int t0, int t1,
-                                             const bf16x8 (&qf)[QK_STEPS], int n_vis, int min_vis,
+                                             const QF& qf, int n_vis, int min_vis,
                                              SegState& st, PageWin& pw) {
   constexpr int LOADS = tile_loads<FP8>();
   const int lane = threadIdx.x & 63;
@@ -812,25 +828,65 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   // QK^T of the tile in buf.  fill(k) runs right after MFMA k: independent VALU
   // work (the previous tile's softmax) that the wave issues while the matrix
   // core is busy; the scheduling barrier keeps each piece in its slot.
+  // fp8 query: A fragment of 64-dim step kk (0..7 latent, 8 RoPE) is 32 bytes
+  // of the lane's row, chunks 4kk + 2h and 4kk + 2h + 1 (RoPE: 2h, 2h + 1), the
+  // same bytes the lane's query fragment holds, so the MFMA pairs them
+  // whatever its internal order of the 64 products.
+  const int s8 = swz_lat_fp8(prow);
+  const int s8r = swz_rope_fp8(prow);
+  auto load_a8 = [&](uint32_t buf, int kk) -> i32x8 {
+    uint32_t o0, o1;
+    if (kk < 8) {
+      o0 = buf + prow * 512 + ((16u * ((2 * h) ^ s8)) ^ (64u * kk));
+      o1 = buf + prow * 512 + ((16u * ((2 * h + 1) ^ s8)) ^ (64u * kk));
+    } else {
+      o0 = buf + ROPE_OFF_FP8 + prow * 64 + 16 * ((2 * h) ^ s8r);
+      o1 = buf + ROPE_OFF_FP8 + prow * 64 + 16 * ((2 * h + 1) ^ s8r);
+    }
+    const u32x4 x = lds_read_b128(smem, o0);
+    const u32x4 y = lds_read_b128(smem, o1);
+    return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+  };
   auto qk = [&](uint32_t buf_in, auto&& fill) -> f32x16 {
     const uint32_t buf = opaque(buf_in);
     f32x16 s;
-    constexpr int GA = 4;  // A fragments read this many steps ahead
-    u32x4 araw[GA];
+    if constexpr (Q8) {
+      // 9 MFMAs of 64 dims; fill() gets two slots per MFMA (0..17)
+      constexpr int GA8 = 2;  // A fragments read this many steps ahead
+      i32x8 araw8[GA8];
 #pragma unroll
-    for (int k = 0; k < GA; ++k) araw[k] = load_a(buf, k);
+      for (int k = 0; k < GA8; ++k) araw8[k] = load_a8(buf, k);
 #pragma unroll
-    for (int k = 0; k < QK_STEPS; ++k) {
-      const u32x4 cur = araw[k % GA];
-      if (k + GA < QK_STEPS) araw[k % GA] = load_a(buf, k + GA);
-      if (k == 0) s = mfma_first_vgpr(to_bf16(cur), qf[k]);
-      else mfma_acc_vgpr(s, to_bf16(cur), qf[k]);
-      fill(k);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < 9; ++k) {
+        const i32x8 cur = araw8[k % GA8];
+        if (k + GA8 < 9) araw8[k % GA8] = load_a8(buf, k + GA8);
+        if (k == 0) s = mfma8_first_vgpr(cur, qf[0]);
+        else mfma8_acc_vgpr(s, cur, qf[k]);
+        fill(2 * k);
+        fill(2 * k + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma8_fence(s);
+      return s;
+    } else {
+      constexpr int GA = 4;  // A fragments read this many steps ahead
+      u32x4 araw[GA];
+#pragma unroll
+      for (int k = 0; k < GA; ++k) araw[k] = load_a(buf, k);
+#pragma unroll
+      for (int k = 0; k < QK_STEPS; ++k) {
+        const u32x4 cur = araw[k % GA];
+        if (k + GA < QK_STEPS) araw[k % GA] = load_a(buf, k + GA);
+        if (k == 0) s = mfma_first_vgpr(to_bf16(cur), qf[k]);
+        else mfma_acc_vgpr(s, to_bf16(cur), qf[k]);
+        fill(k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma_fence(s);
+      return s;
     }
-    mfma_fence(s);
-    return s;
   };
+  static_assert(!Q8 || FP8, "an fp8 query needs the fp8 cache");
   auto no_fill = [](int) {};
 
   // Tile t has landed once at most the DMA ops of the n tiles issued after it
@@ -966,7 +1022,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
         }
       }
       if (ACTIVE) {
-        if (fast && !FP8) {
+        if (fast && (!FP8 || Q8)) {
           const float nm = -st.m_ref;
           s_next = qk(buf_of(t + 1), [&](int k) { fast_piece(s, nm, k); });
         } else if (fast) {
@@ -1038,7 +1094,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
 // reference max (the first visible tile's max) by more than 2^32.  m_seed then
 // holds each lane's observed max as the new reference and the caller runs the
 // segment again, which cannot overflow; O is never rescaled.
-template <bool FP8, int PS>
+template <bool FP8, int PS, bool Q8>
 __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, int b, int pb, int L, int t0, int t1,
                                                 int slot, float& m_seed) {
   const int lane = threadIdx.x & 63;
@@ -1085,22 +1141,36 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
     if (t0 + 2 < t1) issue_tile<FP8, PS>(p, smem, 2 * TILEB, b, L, t0 + 2, pw);
   }
 
-  // Query fragments (B operand): lane holds pair `col`; step kk < 32 covers latent
-  // dims 16kk + 8h .. +8, steps 32..35 RoPE dims 512 + 16(kk-32) + 8h.
-  bf16x8 qf[QK_STEPS];
+  // Query fragments (B operand): lane holds pair `col`.  bf16: step kk < 32
+  // covers latent dims 16kk + 8h .. +8, steps 32..35 RoPE dims 512 + 16(kk-32)
+  // + 8h.  fp8 query: step kk < 9 covers bytes 64kk + 32h .. +32 of the row.
+  constexpr int QN = Q8 ? 9 : QK_STEPS;
+  using QFrag = std::conditional_t<Q8, i32x8, bf16x8>;
+  QFrag qf[QN];
   {
-    const uint16_t* qrow = p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 8 * h;
+    const bool live = valid && active;
+    if constexpr (Q8) {
+      const uint8_t* qrow = (const uint8_t*)p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 32 * h;
 #pragma unroll
-    for (int k = 0; k < QK_STEPS; ++k) {
-      const u32x4 v = (valid && active) ? *(const u32x4*)(qrow + 16 * k) : u32x4{0, 0, 0, 0};
-      qf[k] = __builtin_bit_cast(bf16x8, v);
+      for (int k = 0; k < QN; ++k) {
+        const u32x4 x = live ? *(const u32x4*)(qrow + 64 * k) : u32x4{0, 0, 0, 0};
+        const u32x4 y = live ? *(const u32x4*)(qrow + 64 * k + 16) : u32x4{0, 0, 0, 0};
+        qf[k] = i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+      }
+    } else {
+      const uint16_t* qrow = p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 8 * h;
+#pragma unroll
+      for (int k = 0; k < QN; ++k) {
+        const u32x4 v = live ? *(const u32x4*)(qrow + 16 * k) : u32x4{0, 0, 0, 0};
+        qf[k] = __builtin_bit_cast(bf16x8, v);
+      }
     }
     // Wait for the loads here and redefine the registers through an empty asm,
     // so the compiler sees no load pending on them inside the tile loop (a
     // vmcnt wait there would also drain the tiles' DMA).
     drain_vector_loads();
 #pragma unroll
-    for (int k = 0; k < QK_STEPS; ++k) asm volatile("" : "+v"(qf[k]));
+    for (int k = 0; k < QN; ++k) asm volatile("" : "+v"(qf[k]));
   }
 
   SegState st;
@@ -1111,8 +1181,8 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   st.s_max = -INFINITY;
   st.lsum = 0.f;
   st.ref_ready = __builtin_amdgcn_ballot_w64(m_seed == -INFINITY) == 0;
-  if (active) segment_loop<FP8, PS, true>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
-  else segment_loop<FP8, PS, false>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
+  if (active) segment_loop<FP8, PS, true, Q8>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
+  else segment_loop<FP8, PS, false, Q8>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
 
   // ---- segment end: the largest logit of the segment decides whether some
   // exponential went past the threshold; all waves idle on LDS; one flag per
@@ -1197,7 +1267,7 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
 
 // ---------------------------------------------------------------- decode kernel
 
-template <bool FP8, int PS>
+template <bool FP8, int PS, bool Q8>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(Params p) {
   if (p.bmm1_dev != nullptr) p.scale_log2 = *p.bmm1_dev * LOG2E;
@@ -1274,7 +1344,7 @@ void mla_decode_kernel(Params p) {
     // later segment has a larger g or a larger u
     const int slot = g + u_base + pb;
     float m_seed = -INFINITY;
-    while (!process_segment<FP8, PS>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
+    while (!process_segment<FP8, PS, Q8>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
     }
     x += t1 - t0;
     rel += t1 - t0;
@@ -1565,9 +1635,9 @@ int validate_sparse(const mla_decode_dims_t* d, int32_t top_k) {
   return MLA_OK;
 }
 
-template <bool FP8, int PS>
+template <bool FP8, int PS, bool Q8 = false>
 void launch_decode(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, PS>), dim3(p.grid), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL((mla_decode_kernel<FP8, PS, Q8>), dim3(p.grid), dim3(THREADS), 0, s, p);
 }
 
 }  // namespace
@@ -1627,6 +1697,7 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
                         const mla_decode_dims_t* dims, void* stream, const mla_decode_options_t* opts) {
   const int32_t top_k = opts != nullptr ? opts->sparse_top_k : 0;
   const bool sparse = top_k > 0;
+  const bool q8 = opts != nullptr && opts->q_fp8 != 0;
   if (!q || !kv_cache || !block_tables || (!seq_lens && !sparse) || !out || !workspace || !dims)
     return MLA_ERR_NULL_POINTER;
   if (opts != nullptr && (((uintptr_t)opts->bmm1_scale | (uintptr_t)opts->bmm2_scale | (uintptr_t)opts->sinks |
@@ -1635,9 +1706,10 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   const bool dcp = opts != nullptr && opts->seq_lens_global != nullptr;
   if (dcp && (opts->cp_world < 1 || opts->cp_rank < 0 || opts->cp_rank >= opts->cp_world)) return MLA_ERR_BAD_SHAPE;
   if (dcp && lse == nullptr) return MLA_ERR_NULL_POINTER;
-  if (top_k < 0 || (sparse && dcp)) return MLA_ERR_BAD_SHAPE;
+  if (top_k < 0 || (sparse && dcp) || (sparse && q8)) return MLA_ERR_BAD_SHAPE;
   const int v = sparse ? validate_sparse(dims, top_k) : validate(dims, max_seq_len, max_q_len, qo_indptr != nullptr);
   if (v != MLA_OK) return v;
+  if (q8 && dims->kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_BAD_DTYPE;
   if (((uintptr_t)q | (uintptr_t)kv_cache | (uintptr_t)out | (uintptr_t)workspace) & 15) return MLA_ERR_MISALIGNED;
   if (lse != nullptr && ((uintptr_t)lse & 3)) return MLA_ERR_MISALIGNED;
   int grid = 0;
@@ -1694,6 +1766,12 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   if (ev0 != nullptr) (void)hipEventRecord((hipEvent_t)ev0, s);
   if (sparse) {
     fp8 ? launch_decode<true, 0>(p, s) : launch_decode<false, 0>(p, s);
+  } else if (q8) {
+    switch (dims->page_size) {
+      case 16: launch_decode<true, 16, true>(p, s); break;
+      case 32: launch_decode<true, 32, true>(p, s); break;
+      default: launch_decode<true, 64, true>(p, s); break;
+    }
   } else switch (dims->page_size) {
     case 16: fp8 ? launch_decode<true, 16>(p, s) : launch_decode<false, 16>(p, s); break;
     case 32: fp8 ? launch_decode<true, 32>(p, s) : launch_decode<false, 32>(p, s); break;

@@ -243,6 +243,15 @@ def named_workload(name, poison=True, **overrides):
     return make_workload(name, poison=poison, **spec)
 
 
+def fp8_query_codes(w, inv_q_scale=1.0):
+    """uint8 OCP E4M3FN codes of the workload's query times inv_q_scale, rounded
+    by torch (RNE): the fp8 query a caller with per-tensor q_scale =
+    1 / inv_q_scale would pass (that q_scale then belongs in bmm1_scale)."""
+    import torch
+    q = torch.from_numpy(w.q_bits).view(torch.bfloat16).to(torch.float32) * float(inv_q_scale)
+    return q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def sparse_lists(w, top_k, seed, *, empty_frac=0.0, repeat_frac=0.0, empty_rows=()):
     """Seeded top-k lists for a workload's query rows: int32 [total_q, top_k]
     of flat cache-row ids (page * page_size + slot).

@@ -11,9 +11,10 @@ hand.  This checker re-derives the two rules that matter from the assembly:
     within OPERAND_WAIT wait states before it.
 
 An `s_nop N` counts as N + 1 wait states, every other instruction as one.  The
-rules are the ones the compiler itself applies around v_mfma_f32_32x32x16_bf16
-on gfx950 (it emits 11-12 wait states between such an MFMA and a dependent
-VALU and 2 between a VALU write and an MFMA source read).  Windows are carried
+rules are the ones the compiler itself applies on gfx950: it emits 11-12 wait
+states between v_mfma_f32_32x32x16_bf16 and a dependent VALU, 20 after the
+16-pass v_mfma_f32_32x32x64_f8f6f4, and 2 between a VALU write and an MFMA
+source read.  Windows are carried
 across basic blocks along every branch and fall-through edge (a forward
 dataflow pass to a fixed point), so loop back-edges are covered.
 """
@@ -22,6 +23,8 @@ import re
 
 RESULT_WAIT = 12
 OPERAND_WAIT = 2
+# result windows of MFMAs with more passes than the bf16 32x32x16 one
+RESULT_WAIT_BY_OP = {"v_mfma_f32_32x32x64_f8f6f4": 20}
 
 _REG = re.compile(r"(?<![\w.])([va])(?:\[(\d+):(\d+)\]|(\d+)(?!\w))")
 _LABEL = re.compile(r"^(\.LBB\d+_\d+|\.Ltmp\d+):")
@@ -139,7 +142,7 @@ def _run_block(insts, pending, recent, problems):
             pending = {r: (l - waits, d, a) for r, (l, d, a) in pending.items() if l - waits > 0}
             recent = {r: (l - waits, a) for r, (l, a) in recent.items() if l - waits > 0}
             for r in dregs:
-                pending[r] = (RESULT_WAIT, key, no)
+                pending[r] = (RESULT_WAIT_BY_OP.get(op, RESULT_WAIT), key, no)
             continue
         if op != "s_nop":
             touched = set()

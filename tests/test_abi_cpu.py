@@ -94,6 +94,7 @@ def test_options_struct_and_misaligned_option_pointers():
     assert ctypes.sizeof(binding.MlaOptions) == 48
     assert binding.MlaOptions.sinks.offset == 16
     assert binding.MlaOptions.sparse_top_k.offset == 40
+    assert binding.MlaOptions.q_fp8.offset == 44
     for field in ("bmm1_scale", "bmm2_scale", "sinks"):
         opts = binding.MlaOptions(None, None, None)
         setattr(opts, field, FAKE + 2)
@@ -150,3 +151,16 @@ def test_sparse_options_reject_bad_arguments():
     assert ex(sd(), 0) == NULL                                                  # ... but not in the paged layout
     opts = binding.MlaOptions(None, None, None, None, 1, 0, 65)
     assert binding.mla_decode_paged_ex_workspace_size(sd(), 1, 1, False, opts) == 0
+
+
+def test_fp8_query_option_rejects_bad_combinations():
+    BAD_DTYPE, BAD_SHAPE = 5, 10
+
+    def ex(dims, opts):
+        return binding.mla_decode_paged_ex(FAKE, FAKE, FAKE, FAKE, None, 128, 1, 1.0, 1.0, True, FAKE, None, FAKE,
+                                           1 << 30, dims, opts, stream=0)
+    q8 = binding.MlaOptions(None, None, None, None, 1, 0, 0, 1)
+    assert ex(_dims(kv_dtype=0), q8) == BAD_DTYPE           # fp8 query with a bf16 cache
+    assert ex(_dims(kv_dtype=1), q8) == NO_DEVICE           # fp8 query and fp8 cache: accepted
+    sq8 = binding.MlaOptions(None, None, None, None, 1, 0, 4, 1)
+    assert ex(_dims(kv_dtype=1), sq8) == BAD_SHAPE          # not in the sparse layout

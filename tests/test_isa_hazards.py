@@ -42,7 +42,9 @@ def library_asm(tmp_path_factory):
 @pytest.fixture(scope="module")
 def decode_bodies(library_asm):
     bodies = {n: b for n, b in ih.kernel_bodies(library_asm) if "mla_decode_kernel" in n}
-    assert len(bodies) == 8, sorted(bodies)  # {bf16, fp8} x (page size {16, 32, 64} + the sparse layout)
+    # {bf16, fp8} x (page size {16, 32, 64} + the sparse layout), and the fp8
+    # query kernels (page size {16, 32, 64})
+    assert len(bodies) == 11, sorted(bodies)
     return bodies
 
 
@@ -51,7 +53,8 @@ def test_library_kernels_have_no_mfma_hazards(library_asm, decode_bodies):
     bad = {k: v for k, v in res.items() if v}
     assert not bad, {k: v[:3] for k, v in bad.items()}
     for name, body in decode_bodies.items():
-        assert sum("v_mfma" in l for l in body) >= 68, name  # 36 QK^T + 32 P.V steps per tile
+        # per tile: 36 QK^T + 32 P.V steps (fp8 query: 9 QK^T steps of 64 dims)
+        assert sum("v_mfma" in l for l in body) >= (41 if "Lb1EEEvNS" in name else 68), name
 
 
 def _loop_depths(body):
@@ -120,7 +123,7 @@ def test_checker_accepts_compiler_scheduled_mfma(tmp_path):
 
 def test_checker_finds_planted_hazards(decode_bodies):
     # the fp8, page-size-16 kernel (whose fences guard reads the checker must see)
-    body = next(b for n, b in decode_bodies.items() if "ILb1ELi16E" in n)
+    body = next(b for n, b in decode_bodies.items() if "ILb1ELi16ELb0E" in n)
     assert not ih.check_body(body)
     # a read of an MFMA result right after the MFMA
     i = next(k for k, l in enumerate(body) if "v_mfma" in l)
@@ -141,3 +144,20 @@ def test_checker_finds_planted_hazards(decode_bodies):
         while re.match(r"\s*s_nop", body[j - 1]):
             j -= 1
         assert ih.check_body(body[:j] + [write] + body[i:])
+
+
+def test_checker_knows_the_longer_fp8_mfma_window(decode_bodies):
+    """The fp8 query kernels' v_mfma_f32_32x32x64_f8f6f4 needs 20 wait states
+    before its result is read: the kernels pass, and a read after only the 12
+    that suffice for the bf16 MFMA is flagged."""
+    body = next(b for n, b in decode_bodies.items() if "ILb1ELi64ELb1E" in n)
+    assert not ih.check_body(body)
+    i = next(k for k, l in enumerate(body) if "v_mfma_f32_32x32x64_f8f6f4" in l)
+    dst = body[i].split()[1].rstrip(",")
+    m = re.match(r"v\[(\d+)", dst)
+    read = [f"\ts_nop 7", f"\ts_nop 3", f"\tv_mov_b32_e32 v0, v{m.group(1)}"]
+    assert ih.check_body(body[:i + 1] + read + body[i + 1:])
+    ok = [f"\ts_nop 15", f"\ts_nop 3", f"\tv_mov_b32_e32 v0, v{m.group(1)}"]
+    # (20 wait states: nothing new is flagged at this read)
+    new = set(ih.check_body(body[:i + 1] + ok + body[i + 1:]))
+    assert not any(f"line" in p and "v_mov_b32_e32 v0" in p for p in new)
