@@ -35,9 +35,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s=10.0):
+def cpu_baseline(w, budget_s=10.0, q_codes=None):
     """Time the oracle as it stands on whole requests of w (cycling through the
-    batch) until about budget_s seconds of CPU work have been spent."""
+    batch) until about budget_s seconds of CPU work have been spent (q_codes:
+    the fp8 query codes of an fp8-query workload)."""
     import numpy as np
     import oracle
     try:
@@ -46,6 +47,9 @@ def cpu_baseline(w, budget_s=10.0):
     except Exception:
         threads = os.cpu_count() or 1
     prob = oracle.MlaProblem(**w.oracle_problem_kwargs())
+    if q_codes is not None:
+        prob.q_bits = q_codes
+        prob.q_dtype = "fp8_e4m3fn"
     calls, tokens = 0, 0
     t0 = time.perf_counter()
     while True:
@@ -125,19 +129,21 @@ def time_steps(step, steps, warmup):
     return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
-def roofline(counts, kern_ms, name):
+def roofline(counts, kern_ms, name, q8=False):
     """The decode kernel against its bound: HBM if its algorithmic bytes take
-    longer at peak than its algorithmic flops at the bf16 MFMA peak."""
-    from paged_mla_decode_03_amd.metrics import PEAK_HBM_GBS, PEAK_MFMA_TFLOPS
+    longer at peak than its algorithmic flops at the MFMA peak (bf16; with an
+    fp8 query, QK^T at the fp8 peak and P.V at the bf16 one)."""
+    from paged_mla_decode_03_amd.metrics import PEAK_HBM_GBS, PEAK_MFMA_TFLOPS, mixed_mfma_peak
+    peak_mfma = mixed_mfma_peak() if q8 else PEAK_MFMA_TFLOPS["bf16"]
     t_hbm = counts["bytes"] / (PEAK_HBM_GBS * 1e9)
-    t_mfma = counts["flops"] / (PEAK_MFMA_TFLOPS["bf16"] * 1e12)
+    t_mfma = counts["flops"] / (peak_mfma * 1e12)
     if t_hbm >= t_mfma:
         achieved = counts["bytes"] / (kern_ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS, "traffic": profiled_traffic(name)}
     achieved = counts["flops"] / (kern_ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS["bf16"], "unit": "TFLOP/s",
-            "frac": achieved / PEAK_MFMA_TFLOPS["bf16"], "traffic": profiled_traffic(name)}
+    return {"bound": "mfma", "achieved": achieved, "peak": peak_mfma, "unit": "TFLOP/s",
+            "frac": achieved / peak_mfma, "traffic": profiled_traffic(name)}
 
 
 def sparse_cpu_baseline(w, lists, budget_s=10.0):
@@ -236,13 +242,18 @@ def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
 def run_workload(name, steps, warmup, want_cpu, rotate=3):
     import torch
     from paged_mla_decode_03_amd import binding
-    from paged_mla_decode_03_amd.inputs import named_workload, to_device_tensors, WORKLOADS
+    from paged_mla_decode_03_amd.inputs import (named_workload, to_device_tensors, WORKLOADS, Q8_WORKLOADS,
+                                                fp8_query_codes)
     from paged_mla_decode_03_amd.metrics import counts_for_workload
 
     log(f"[bench] generating workload {name}")
-    w = named_workload(name, poison=False)
+    q8 = name in Q8_WORKLOADS
+    base = Q8_WORKLOADS.get(name, name)
+    w = named_workload(base, poison=False)
     counts = counts_for_workload(w)
     t = to_device_tensors(w, "cuda")
+    if q8:
+        t["q"] = torch.from_numpy(fp8_query_codes(w)).view(torch.float8_e4m3fn).cuda()
     B, H = w.batch, w.num_heads
     q = t["q"] if w.qo_indptr is not None else t["q"].view(B, w.q_len_fixed, H, 576)
     max_q = w.max_q_len if w.qo_indptr is not None else None
@@ -266,11 +277,12 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
     arg_sets = [(qq.data_ptr(), kv.data_ptr(), t["block_tables"].data_ptr(), t["seq_lens"].data_ptr(),
                  None if t["qo_indptr"] is None else t["qo_indptr"].data_ptr(), w.max_seq_len, max_q_len,
                  w.bmm1_scale, w.bmm2_scale, w.causal, out.data_ptr(), None if lse is None else lse.data_ptr(),
-                 ws.data_ptr(), nbytes, dims, stream) for qq, kv in zip(qs, kvs)]
+                 ws.data_ptr(), nbytes, dims) for qq, kv in zip(qs, kvs)]
+    opts = binding.MlaOptions(None, None, None, None, 1, 0, 0, 1) if q8 else None
     n_step = [0]
 
     def step():
-        rc = binding.mla_decode_paged(*arg_sets[n_step[0] % len(arg_sets)])
+        rc = binding.mla_decode_paged_ex(*arg_sets[n_step[0] % len(arg_sets)], opts, stream=stream)
         n_step[0] += 1
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
@@ -278,8 +290,10 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
     ms_step, kern_ms = time_steps(step, steps, warmup)
     kv_bytes_per = 2 if w.kv_dtype == "bf16" else 1
     dtype = "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma"
-    roof = roofline(counts, kern_ms, name)
-    spec = WORKLOADS[name]
+    roof = roofline(counts, kern_ms, name, q8=q8)
+    if q8:
+        dtype = "fp8 QK^T / bf16 P.V"
+    spec = WORKLOADS[base]
     res = {
         "metric": METRIC,
         "value": counts["kv_tokens"] / (ms_step * 1e-3),
@@ -292,8 +306,9 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if kv_bytes_per == 2 else dtype,
-        "data": f"synthetic (seeded N(0,1) q/kv, shuffled pages; {max(1, rotate)} cache copies rotated across steps)",
-        "config": {"workload": name, "batch": B, "heads": H,
+        "data": f"synthetic (seeded N(0,1) q/kv, shuffled pages; {max(1, rotate)} cache copies rotated across steps)"
+                + ("; query rounded to fp8 E4M3FN, q_scale 1" if q8 else ""),
+        "config": {"workload": name, "batch": B, "heads": H, **({"q_dtype": "fp8_e4m3fn"} if q8 else {}),
                    "q_len": spec.get("q_len") if "q_len_range" not in spec else list(spec["q_len_range"]),
                    "seq_lens": list(spec["seq_len_range"]) if "seq_len_range" in spec else
                    (list(spec["seq_len_loguniform"]) if "seq_len_loguniform" in spec else spec.get("seq_lens")),
@@ -307,7 +322,7 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
     }
     if want_cpu:
         log("[bench] cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"] = cpu_baseline(w, q_codes=fp8_query_codes(w) if q8 else None)
     return res
 
 
@@ -335,7 +350,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    from paged_mla_decode_03_amd.inputs import WORKLOAD_ORDER, SPARSE_WORKLOADS
+    from paged_mla_decode_03_amd.inputs import WORKLOAD_ORDER, SPARSE_WORKLOADS, Q8_WORKLOADS
 
     def run(name, want_cpu):
         fn = run_sparse_workload if name in SPARSE_WORKLOADS else run_workload
@@ -343,7 +358,7 @@ def main():
 
     res = run(args.workload, not args.no_cpu_baseline)
     if args.all:
-        for name in WORKLOAD_ORDER + list(SPARSE_WORKLOADS):
+        for name in WORKLOAD_ORDER + list(SPARSE_WORKLOADS) + list(Q8_WORKLOADS):
             if name == args.workload:
                 continue
             log("[bench-extra] " + json.dumps(run(name, False)))

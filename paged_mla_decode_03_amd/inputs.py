@@ -217,6 +217,10 @@ WORKLOADS = {
 
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# fp8-query variants (mla_decode_options_t.q_fp8): the named workload with its
+# query rounded to E4M3FN (q_scale 1, so bmm1 is unchanged).
+Q8_WORKLOADS = {"fp8_long_context_q8": "fp8_long_context"}
+
 # Sparse top-k decode (the layout of mla_decode_options_t.sparse_top_k): a
 # DeepSeek-shaped batch whose every query row attends to a top-k selection of
 # its request.  The pages give no sparse configuration; this one takes the

@@ -27,6 +27,16 @@ D_V = 512
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 
+# Share of the decode flops in QK^T (576 of the 1088 dims per visible pair):
+# with an fp8 query that part runs at the fp8 peak and P.V at the bf16 one.
+QK_SHARE = 576.0 / 1088.0
+
+
+def mixed_mfma_peak():
+    """TFLOP/s of the whole decode at the matrix-core peaks when QK^T is fp8 and
+    P.V bf16: F / (F_qk / P_fp8 + F_pv / P_bf16)."""
+    return 1.0 / (QK_SHARE / PEAK_MFMA_TFLOPS["fp8"] + (1.0 - QK_SHARE) / PEAK_MFMA_TFLOPS["bf16"])
+
 
 def workload_counts(seq_lens, q_lens, num_heads, page_size, kv_bytes, causal, want_lse, packed):
     L = np.asarray(seq_lens, dtype=np.int64)
