@@ -337,45 +337,66 @@ __device__ __forceinline__ int request_tiles(const Params& p, int b) { return ma
 
 __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* scan) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
   const int B = p.batch;
+  constexpr int PER_MAX = (MLA_MAX_BATCH + THREADS - 1) / THREADS;
   const int per = (B + THREADS - 1) / THREADS;
   const int b0 = min(B, tid * per);
-  const int b1 = min(B, b0 + per);
+  // this thread's requests, kept in registers for the second pass
+  int t_b[PER_MAX], u_b[PER_MAX];
   int tiles = 0, units = 0;
-  for (int b = b0; b < b1; ++b) {
-    int r0;
-    const int qb = request_rows(p, b, r0);
-    const int u = request_units(p, qb);
+#pragma unroll
+  for (int i = 0; i < PER_MAX; ++i) {
+    int t = 0, u = 0;
+    if (i < per && b0 + i < B) {
+      int r0;
+      u = request_units(p, request_rows(p, b0 + i, r0));
+      t = u * request_tiles(p, b0 + i);
+    }
+    t_b[i] = t;
+    u_b[i] = u;
+    tiles += t;
     units += u;
-    tiles += u * request_tiles(p, b);
   }
-  int* scan_t = scan;
-  int* scan_u = scan + THREADS;
-  scan_t[tid] = tiles;
-  scan_u[tid] = units;
+  // inclusive prefix sums: within each wave by shuffles, then the four wave
+  // totals through LDS (one barrier)
+  int st = tiles, su = units;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int vt = __shfl_up(st, off, 64);
+    const int vu = __shfl_up(su, off, 64);
+    if (lane >= off) {
+      st += vt;
+      su += vu;
+    }
+  }
+  int* wave_t = scan;
+  int* wave_u = scan + WAVES;
+  if (lane == 63) {
+    wave_t[w] = st;
+    wave_u[w] = su;
+  }
   __syncthreads();
-  for (int off = 1; off < THREADS; off <<= 1) {
-    const int vt = tid >= off ? scan_t[tid - off] : 0;
-    const int vu = tid >= off ? scan_u[tid - off] : 0;
-    __syncthreads();
-    scan_t[tid] += vt;
-    scan_u[tid] += vu;
-    __syncthreads();
+  int base_t = 0, base_u = 0;
+  for (int k = 0; k < w; ++k) {
+    base_t += wave_t[k];
+    base_u += wave_u[k];
   }
-  int run_t = scan_t[tid] - tiles;
-  int run_u = scan_u[tid] - units;
-  for (int b = b0; b < b1; ++b) {
-    int r0;
-    const int qb = request_rows(p, b, r0);
-    const int u = request_units(p, qb);
-    tile_off[b] = run_t;
-    unit_off[b] = run_u;
-    run_t += u * request_tiles(p, b);
-    run_u += u;
+  int run_t = base_t + st - tiles;
+  int run_u = base_u + su - units;
+#pragma unroll
+  for (int i = 0; i < PER_MAX; ++i) {
+    if (i < per && b0 + i < B) {
+      tile_off[b0 + i] = run_t;
+      unit_off[b0 + i] = run_u;
+    }
+    run_t += t_b[i];
+    run_u += u_b[i];
   }
   if (tid == THREADS - 1) {
-    tile_off[B] = scan_t[THREADS - 1];
-    unit_off[B] = scan_u[THREADS - 1];
+    tile_off[B] = base_t + st;
+    unit_off[B] = base_u + su;
   }
   __syncthreads();
 }
