@@ -83,3 +83,29 @@ def test_fp8_query_reference_restart():
     w = make_workload("q8r", seed=84, batch=3, seq_len_range=(600, 2000), num_heads=32, q_len=2, page_size=32,
                       kv_dtype="fp8_e4m3fn", bmm1_scale=1.0, causal=True, want_lse=True)
     _run_and_check(w, what="restart")
+
+
+def test_full_size_benched_workload_sampled():
+    """fp8_long_context with an fp8 query at full size (8 requests of 64K-128K
+    rows), in the launch the benchmark times, checked on sampled requests."""
+    from paged_mla_decode_03_amd.inputs import named_workload, to_device_tensors
+    w = named_workload("fp8_long_context", poison=True)
+    codes = fp8_query_codes(w)
+    t = to_device_tensors(w, "cuda")
+    q = torch.from_numpy(codes).view(torch.float8_e4m3fn).cuda().view(w.batch, w.q_len_fixed, w.num_heads, 576)
+    ws = torch.empty(binding.workspace_bytes_for(q, t["kv"], t["block_tables"], t["seq_lens"], w.max_seq_len,
+                                                 return_lse=True), dtype=torch.uint8, device="cuda")
+    o, l = binding.decode(q, t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, return_lse=True,
+                          bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale, causal=w.causal)
+    torch.cuda.synchronize()
+    prob = oracle.MlaProblem(**w.oracle_problem_kwargs())
+    prob.q_bits = codes
+    prob.q_dtype = "fp8_e4m3fn"
+    reqs = [0, int(np.argmax(w.seq_lens)), w.batch - 1]
+    ref_o, ref_l = oracle.reference_decode(prob, requests=reqs)
+    rows = np.concatenate([np.arange(b * 2, b * 2 + 2) for b in reqs])
+    H = w.num_heads
+    got_o = o.float().reshape(w.total_q, H, 512).cpu().numpy()[rows]
+    got_l = l.reshape(w.total_q, H).cpu().numpy()[rows]
+    check_close(got_o, ref_o[rows], "q8 full-size out")
+    check_close(got_l, ref_l[rows], "q8 full-size lse")

@@ -112,3 +112,17 @@ def test_full_in_order_lists_equal_the_dense_path():
     check_close(o_s.float().cpu().numpy(), o_d.float().reshape(2, 128, 512).cpu().numpy().astype(np.float64),
                 "sparse vs dense out")
     check_close(l_s.cpu().numpy(), l_d.reshape(2, 128).cpu().numpy().astype(np.float64), "sparse vs dense lse")
+
+
+def test_full_size_benched_workload_sampled_rows():
+    """The benched sparse workload at full size (64 rows, top-k 2048, 128
+    heads), in the launch the benchmark times, checked on sampled rows."""
+    from paged_mla_decode_03_amd.inputs import named_sparse_workload
+    w, lists = named_sparse_workload("sparse_topk_decode", poison=True)
+    o, l = _run(w, lists)
+    rows = [0, 17, 40, 63]
+    ref_o, ref_l = reference_sparse_decode(w.q_bits[rows], w.kv_bits, w.kv_dtype, lists[rows], w.bmm1_scale,
+                                           w.bmm2_scale)
+    rms, _ = check_close(o.float().cpu().numpy()[rows], ref_o, "sparse full-size out")
+    assert rms < 5e-3
+    check_close(l.cpu().numpy()[rows], ref_l, "sparse full-size lse")
