@@ -45,7 +45,8 @@ enum {
   MLA_ERR_BAD_Q_LEN = 8,         /* max_q_len < 1, fixed launch with q_len_fixed != max_q_len,
                                     or total_q inconsistent with a fixed launch */
   MLA_ERR_BAD_BLOCK_TABLE = 9,   /* block_table_stride * page_size < max_seq_len */
-  MLA_ERR_BAD_SHAPE = 10,        /* batch out of [1, MLA_MAX_BATCH], max_seq_len < 1, num_pages < 1 */
+  MLA_ERR_BAD_SHAPE = 10,        /* batch out of [1, MLA_MAX_BATCH], max_seq_len < 1, num_pages < 1,
+                                    total_q * num_heads >= 2^31 - 4 */
   MLA_ERR_HIP = 11,              /* the HIP runtime reported an error at launch */
   MLA_ERR_NO_DEVICE = 12         /* no usable gfx950 device is current */
 };

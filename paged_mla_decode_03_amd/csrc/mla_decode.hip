@@ -1618,6 +1618,8 @@ WsLayout workspace_layout(int grid, int64_t units) {
 // Checks shared by the paged and the sparse layouts.
 int validate_common(const mla_decode_dims_t* d) {
   if (d->num_heads <= 0 || d->num_heads % 16 != 0) return MLA_ERR_BAD_HEADS;
+  // (row, head) items are counted in 32 bits by the merge launch
+  if ((int64_t)d->total_q * d->num_heads >= ((int64_t)1 << 31) - 4) return MLA_ERR_BAD_SHAPE;
   if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64) return MLA_ERR_BAD_PAGE_SIZE;
   if (d->kv_lora_rank != 512 || d->qk_rope_head_dim != 64) return MLA_ERR_BAD_HEAD_DIMS;
   if (d->kv_dtype != MLA_KV_BF16 && d->kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_BAD_DTYPE;

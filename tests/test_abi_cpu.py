@@ -77,6 +77,7 @@ def test_null_pointers(over, code):
     (dict(), dict(max_q_len=0), 8), (dict(q_len_fixed=2), {}, 8), (dict(total_q=3), {}, 8),
     (dict(block_table_stride=3), {}, 9),
     (dict(batch=0), {}, 10), (dict(batch=100000), {}, 10), (dict(), dict(max_seq_len=0), 10),
+    (dict(batch=1000, q_len_fixed=2 ** 19, total_q=1000 * 2 ** 19, num_heads=16), dict(max_q_len=2 ** 19), 10),
 ])
 def test_bad_arguments(dims_over, call_over, code):
     assert _call(_dims(**dims_over), **call_over) == code
