@@ -161,3 +161,11 @@ def test_checker_knows_the_longer_fp8_mfma_window(decode_bodies):
     # (20 wait states: nothing new is flagged at this read)
     new = set(ih.check_body(body[:i + 1] + ok + body[i + 1:]))
     assert not any(f"line" in p and "v_mov_b32_e32 v0" in p for p in new)
+
+
+def test_no_scalar_cache_writes(library_asm):
+    """Device code never writes through the scalar data cache: no scalar
+    stores, scalar atomics or scalar-cache write-back/discard anywhere."""
+    bad = [l.strip() for l in library_asm.splitlines()
+           if re.match(r"\s*s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb|dcache_discard)", l)]
+    assert not bad, bad[:5]
