@@ -10,31 +10,41 @@
 // every pair of the request.
 //
 // Kernel design (one 4-wave workgroup per compute unit, persistent):
-//   * Work plan, on device: every workgroup scans seq_lens / qo_indptr into LDS
+//   * Work plan, on device: every workgroup scans seq_lens / qo_indptr
 //     (tiles of 32 KV rows per "unit" = request x block of 128 (row, head)
-//     pairs), then owns an equal, contiguous range of the linearised
-//     (unit, tile) space.  A unit cut by range boundaries is written as partials
-//     and merged by a second kernel.  No device-to-host read anywhere.
-//   * Each wave owns 32 pairs with all 576 query dims in VGPRs (MFMA B operand)
-//     and all 512 output dims in accumulators, so a KV tile is read from HBM
-//     once per unit and no logits are exchanged between waves.
+//     pairs), then owns an equal, contiguous range of a cost space that counts
+//     every tile and charges each segment start.  A unit cut by range
+//     boundaries is written as partials and merged by a second kernel.  No
+//     device-to-host read anywhere.
+//   * QK^T: wave w owns 32 pairs with all 576 query dims in VGPRs (MFMA B
+//     operand) and computes S^T[32 tokens x 32 pairs] on
+//     v_mfma_f32_32x32x16_bf16 with the KV tile as the A operand (rows permuted
+//     so the result lands in the layout P.V needs).  The loop runs one tile
+//     ahead: the next tile's QK^T MFMAs carry the current tile's softmax
+//     between them.
+//   * P.V: waves 2g and 2g+1 exchange their bf16 P through LDS; each then
+//     accumulates both waves' 64 pairs over one half of the 512 output dims in
+//     AGPRs (O^T += V^T . P^T), so every V^T fragment (ds_read_b64_tr_b16, or
+//     ds_read_b64_tr_b8 for fp8) feeds two MFMAs.  A tile crosses HBM once per
+//     unit and no logits move between waves.
 //   * Loader: each wave streams 8 rows of a tile straight into LDS with
-//     global_load_lds_dwordx4 (16 B per lane; the page base is wave-uniform);
-//     a 4-buffer ring keeps two tiles in flight; rows past seq_len are never
-//     loaded and are zero-filled instead, so NaN in unused slots cannot leak.
-//     16-byte chunks are XOR-swizzled by row to keep LDS reads conflict-free.
-//   * QK^T: S^T[32 tokens x 32 pairs] per wave on v_mfma_f32_32x32x16_bf16 with
-//     the KV tile as the A operand (rows permuted so the result lands directly in
-//     the B-operand layout P.V needs); the next tile's QK^T is issued before the
-//     current tile's softmax so the matrix cores run under the VALU work.
+//     global_load_lds_dwordx4; a 4-buffer ring keeps two tiles in flight; rows
+//     past seq_len are never loaded and are zero-filled instead, so NaN in
+//     unused slots cannot leak.  16-byte chunks are XOR-swizzled by row to keep
+//     LDS reads conflict-free.  Page ids come from a block-table window held in
+//     VGPRs.
 //   * Softmax: exp2 domain (log2 e folded into bmm1), one pair per lane column;
 //     logits are taken relative to a per-pair reference max fixed by the first
 //     visible tile; a logit beyond it by more than 2^32 restarts the segment with
 //     the observed max (never happens for sane inputs; keeps O free of rescales).
-//   * P.V: O^T[512 x 32 pairs] += V^T . P^T on the same MFMA; V^T fragments come
-//     from LDS through ds_read_b64_tr_b16 (bf16) / ds_read_b64_tr_b8 (fp8).
 //   * fp8 E4M3FN KV is converted exactly to bf16 in registers (v_cvt_pk_f32_fp8),
-//     so the MFMA path is the same and scales only enter through bmm1/bmm2.
+//     so the MFMA path is the same and scales only enter through bmm1/bmm2.  With
+//     an fp8 query as well, QK^T runs on v_mfma_f32_32x32x64_f8f6f4 instead.
+//   * Options (mla_decode_paged_ex): device-resident scales, per-head attention
+//     sinks (one more softmax term, applied in the merge), a sequence-sharded
+//     partial mode (causal limits from global lengths), and a sparse top-k
+//     layout in which each query row attends to the cache rows its list names
+//     (list entries fetched into LDS two tiles ahead of the rows).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
