@@ -237,25 +237,17 @@ __device__ __forceinline__ float sum_halves(float v) {
 }
 
 // 8 E4M3FN bytes -> 8 bf16 (exact: every E4M3FN value is a bf16 value).
-// Byte j of (lo, hi) becomes element j.  v_cvt_pk_f32_fp8 widens two codes to
-// f32, v_cvt_pk_bf16_f32 narrows the pair back without rounding error.
+// Byte j of (lo, hi) becomes element j.  gfx950's v_cvt_scalef32_pk_bf16_fp8
+// widens two codes (bytes 0-1, or 2-3 with the word select) straight to bf16;
+// with a scale of 1 it is the plain conversion.  Four instructions per eight
+// codes, half of what a detour through f32 costs.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  bf16x8 r;
-  const uint32_t src[2] = {lo, hi};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const f32x2 f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)src[i], false);
-    const f32x2 f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)src[i], true);
-    const bf16x2 a = __builtin_convertvector(f01, bf16x2);
-    const bf16x2 c = __builtin_convertvector(f23, bf16x2);
-    r[4 * i + 0] = a[0];
-    r[4 * i + 1] = a[1];
-    r[4 * i + 2] = c[0];
-    r[4 * i + 3] = c[1];
-  }
-  return r;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // ---------------------------------------------------------------- matrix-core ops
