@@ -242,6 +242,7 @@ __device__ __forceinline__ float sum_halves(float v) {
 // with a scale of 1 it is the plain conversion.  Four instructions per eight
 // codes, half of what a detour through f32 costs.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false);
   const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true);
@@ -756,10 +757,15 @@ struct SegState {
   bool ref_ready;  // wave-uniform: every lane's m_ref is set
 };
 
-template <bool FP8, int PS, bool ACTIVE, bool Q8, typename QF>
+// Query modes (QM): 0 = bf16 query on the bf16 MFMA (fp8 cache rows widened);
+// 1 = fp8 query codes on the fp8 MFMA; 2 = bf16 query split into two fp8 terms
+// (q 2^e = q_hi + q_lo) on the fp8 MFMA, for an fp8 cache.  c is the logit
+// scale in log2 units of the lane's scores (mode 2: divided by 2^e).
+template <bool FP8, int PS, bool ACTIVE, int QM, typename QF>
 __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int b, int L, int t0, int t1,
-                                             const QF& qf, int n_vis, int min_vis,
+                                             const QF& qf, float c, int n_vis, int min_vis,
                                              SegState& st, PageWin& pw) {
+  constexpr bool Q8 = QM != 0;
   constexpr int LOADS = tile_loads<FP8>();
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -874,7 +880,8 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     const uint32_t buf = opaque(buf_in);
     f32x16 s;
     if constexpr (Q8) {
-      // 9 MFMAs of 64 dims; fill() gets two slots per MFMA (0..17)
+      // 9 MFMAs of 64 dims (split query: 9 pairs, high term then low term);
+      // fill() gets two slots per step (0..17)
       constexpr int GA8 = 2;  // A fragments read this many steps ahead
       i32x8 araw8[GA8];
 #pragma unroll
@@ -886,6 +893,11 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
         if (k == 0) s = mfma8_first_vgpr(cur, qf[0]);
         else mfma8_acc_vgpr(s, cur, qf[k]);
         fill(2 * k);
+        if constexpr (QM == 2) {
+          // the low term of the split query, back to back on the same accumulator
+          __builtin_amdgcn_sched_barrier(0);
+          mfma8_acc_vgpr(s, cur, qf[9 + k]);
+        }
         fill(2 * k + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -925,7 +937,6 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     else wait_vmcnt<2 * PER_TILE>();
   };
 
-  const float c = p.scale_log2;
   const bool c_pos = c > 0.f;
 
   // ---------------- softmax (exp2 domain) of one tile's scores s; value k is
@@ -1117,7 +1128,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
 // reference max (the first visible tile's max) by more than 2^32.  m_seed then
 // holds each lane's observed max as the new reference and the caller runs the
 // segment again, which cannot overflow; O is never rescaled.
-template <bool FP8, int PS, bool Q8>
+template <bool FP8, int PS, int QM>
 __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, int b, int pb, int L, int t0, int t1,
                                                 int slot, float& m_seed) {
   const int lane = threadIdx.x & 63;
@@ -1167,12 +1178,69 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   // Query fragments (B operand): lane holds pair `col`.  bf16: step kk < 32
   // covers latent dims 16kk + 8h .. +8, steps 32..35 RoPE dims 512 + 16(kk-32)
   // + 8h.  fp8 query: step kk < 9 covers bytes 64kk + 32h .. +32 of the row.
-  constexpr int QN = Q8 ? 9 : QK_STEPS;
+  constexpr bool Q8 = QM != 0;
+  constexpr int QN = QM == 2 ? 18 : Q8 ? 9 : QK_STEPS;
   using QFrag = std::conditional_t<Q8, i32x8, bf16x8>;
   QFrag qf[QN];
+  float c = p.scale_log2;
   {
     const bool live = valid && active;
-    if constexpr (Q8) {
+    if constexpr (QM == 2) {
+      // Split query: fragment k < 9 is dims 64k + 32h .. +32 of the row (the
+      // fp8 query's layout), qf[k] holding q_hi and qf[9 + k] q_lo of
+      // q 2^e = q_hi + q_lo, with 2^e putting the pair's largest |q| in
+      // [128, 256).  A bf16 value has 8 significant bits: q_hi keeps the top
+      // four, the remainder has at most four and is exact in E4M3 unless it
+      // falls below E4M3's subnormal step 2^-9 (only for |q 2^e| < 2^-2, i.e.
+      // elements under 2^-9 of the pair's largest), where the error is at most
+      // 2^-10, i.e. 2^-17 of the pair's largest.  The scores come out times 2^e,
+      // which the lane's c takes back out.  The row is read twice (max, then
+      // split) so that the raw values never sit beside the fragments.
+      const uint16_t* qrow = p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 32 * h;
+      float amax = 0.f;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = live ? *(const u32x4*)(qrow + 64 * k + 8 * j) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(v[i] & 0xffff0000u)));
+          }
+        }
+      }
+      amax = max_halves(amax);
+      const int e = 8 - __builtin_amdgcn_frexp_expf(amax);
+      c = __builtin_amdgcn_ldexpf(p.scale_log2, -e);
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        i32x8 hi8, lo8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 v = live ? *(const u32x4*)(qrow + 64 * k + 8 * j) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2) {
+            // word 2j + i2 holds dims 8j + 4i2 .. +4: values v[2i2] (bytes 0-1)
+            // and v[2i2 + 1] (bytes 2-3), each a pair of bf16
+            const float a0 = __builtin_amdgcn_ldexpf(__uint_as_float(v[2 * i2] << 16), e);
+            const float b0 = __builtin_amdgcn_ldexpf(__uint_as_float(v[2 * i2] & 0xffff0000u), e);
+            const float a1 = __builtin_amdgcn_ldexpf(__uint_as_float(v[2 * i2 + 1] << 16), e);
+            const float b1 = __builtin_amdgcn_ldexpf(__uint_as_float(v[2 * i2 + 1] & 0xffff0000u), e);
+            int hw = __builtin_amdgcn_cvt_pk_fp8_f32(a0, b0, 0, false);
+            hw = __builtin_amdgcn_cvt_pk_fp8_f32(a1, b1, hw, true);
+            const f32x2 r0 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+            const f32x2 r1 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+            int lw = __builtin_amdgcn_cvt_pk_fp8_f32(a0 - r0[0], b0 - r0[1], 0, false);
+            lw = __builtin_amdgcn_cvt_pk_fp8_f32(a1 - r1[0], b1 - r1[1], lw, true);
+            hi8[2 * j + i2] = hw;
+            lo8[2 * j + i2] = lw;
+          }
+        }
+        qf[k] = hi8;
+        qf[9 + k] = lo8;
+      }
+    } else if constexpr (Q8) {
       const uint8_t* qrow = (const uint8_t*)p.q + ((size_t)(r0 + qi) * H + head) * D_QK + 32 * h;
 #pragma unroll
       for (int k = 0; k < QN; ++k) {
@@ -1204,13 +1272,13 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   st.s_max = -INFINITY;
   st.lsum = 0.f;
   st.ref_ready = __builtin_amdgcn_ballot_w64(m_seed == -INFINITY) == 0;
-  if (active) segment_loop<FP8, PS, true, Q8>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
-  else segment_loop<FP8, PS, false, Q8>(p, smem, b, L, t0, t1, qf, n_vis, min_vis, st, pw);
+  if (active) segment_loop<FP8, PS, true, QM>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
+  else segment_loop<FP8, PS, false, QM>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
 
   // ---- segment end: the largest logit of the segment decides whether some
   // exponential went past the threshold; all waves idle on LDS; one flag per
   // wave says "redo"
-  const float fast_max = (st.s_max == -INFINITY) ? -INFINITY : max_halves(st.s_max) * p.scale_log2;
+  const float fast_max = (st.s_max == -INFINITY) ? -INFINITY : max_halves(st.s_max) * c;
   const float m_max = fmaxf(st.m_max, fast_max);
   const bool over = m_max > st.m_ref + RESCALE_THRESHOLD;
   int* flags = (int*)(smem + FLAGS_OFF);
@@ -1290,7 +1358,7 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
 
 // ---------------------------------------------------------------- decode kernel
 
-template <bool FP8, int PS, bool Q8>
+template <bool FP8, int PS, int QM>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_decode_kernel(Params p) {
   if (p.bmm1_dev != nullptr) p.scale_log2 = *p.bmm1_dev * LOG2E;
@@ -1367,7 +1435,7 @@ void mla_decode_kernel(Params p) {
     // later segment has a larger g or a larger u
     const int slot = g + u_base + pb;
     float m_seed = -INFINITY;
-    while (!process_segment<FP8, PS, Q8>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
+    while (!process_segment<FP8, PS, QM>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
     }
     x += t1 - t0;
     rel += t1 - t0;
@@ -1660,9 +1728,9 @@ int validate_sparse(const mla_decode_dims_t* d, int32_t top_k) {
   return MLA_OK;
 }
 
-template <bool FP8, int PS, bool Q8 = false>
+template <bool FP8, int PS, int QM>
 void launch_decode(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL((mla_decode_kernel<FP8, PS, Q8>), dim3(p.grid), dim3(THREADS), 0, s, p);
+  hipLaunchKernelGGL((mla_decode_kernel<FP8, PS, QM>), dim3(p.grid), dim3(THREADS), 0, s, p);
 }
 
 }  // namespace
@@ -1789,18 +1857,21 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   void* ev0 = g_ev_start.load(std::memory_order_relaxed);
   void* ev1 = g_ev_stop.load(std::memory_order_relaxed);
   if (ev0 != nullptr) (void)hipEventRecord((hipEvent_t)ev0, s);
+  // fp8 cache: an fp8 query runs as given (mode 1), a bf16 query as two fp8
+  // terms (mode 2); the sparse gather keeps the widened bf16 path (mode 0)
   if (sparse) {
-    fp8 ? launch_decode<true, 0>(p, s) : launch_decode<false, 0>(p, s);
-  } else if (q8) {
+    fp8 ? launch_decode<true, 0, 0>(p, s) : launch_decode<false, 0, 0>(p, s);
+  } else if (fp8) {
+    const int qm = q8 ? 1 : 2;
     switch (dims->page_size) {
-      case 16: launch_decode<true, 16, true>(p, s); break;
-      case 32: launch_decode<true, 32, true>(p, s); break;
-      default: launch_decode<true, 64, true>(p, s); break;
+      case 16: qm == 1 ? launch_decode<true, 16, 1>(p, s) : launch_decode<true, 16, 2>(p, s); break;
+      case 32: qm == 1 ? launch_decode<true, 32, 1>(p, s) : launch_decode<true, 32, 2>(p, s); break;
+      default: qm == 1 ? launch_decode<true, 64, 1>(p, s) : launch_decode<true, 64, 2>(p, s); break;
     }
   } else switch (dims->page_size) {
-    case 16: fp8 ? launch_decode<true, 16>(p, s) : launch_decode<false, 16>(p, s); break;
-    case 32: fp8 ? launch_decode<true, 32>(p, s) : launch_decode<false, 32>(p, s); break;
-    default: fp8 ? launch_decode<true, 64>(p, s) : launch_decode<false, 64>(p, s); break;
+    case 16: launch_decode<false, 16, 0>(p, s); break;
+    case 32: launch_decode<false, 32, 0>(p, s); break;
+    default: launch_decode<false, 64, 0>(p, s); break;
   }
   if (ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev1, s);
   const int items = dims->total_q * dims->num_heads;

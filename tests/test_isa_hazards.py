@@ -42,8 +42,9 @@ def library_asm(tmp_path_factory):
 @pytest.fixture(scope="module")
 def decode_bodies(library_asm):
     bodies = {n: b for n, b in ih.kernel_bodies(library_asm) if "mla_decode_kernel" in n}
-    # {bf16, fp8} x (page size {16, 32, 64} + the sparse layout), and the fp8
-    # query kernels (page size {16, 32, 64})
+    # bf16 cache x (page size {16, 32, 64} + the sparse layout), the fp8 cache's
+    # sparse kernel (widened rows), and for the fp8 cache at page size
+    # {16, 32, 64} the split bf16 query and the fp8 query kernels
     assert len(bodies) == 11, sorted(bodies)
     return bodies
 
@@ -53,8 +54,10 @@ def test_library_kernels_have_no_mfma_hazards(library_asm, decode_bodies):
     bad = {k: v for k, v in res.items() if v}
     assert not bad, {k: v[:3] for k, v in bad.items()}
     for name, body in decode_bodies.items():
-        # per tile: 36 QK^T + 32 P.V steps (fp8 query: 9 QK^T steps of 64 dims)
-        assert sum("v_mfma" in l for l in body) >= (41 if "Lb1EEEvNS" in name else 68), name
+        # per tile: 36 QK^T + 32 P.V steps (fp8 query: 9 QK^T steps of 64 dims;
+        # split query: 9 pairs of them)
+        need = 41 if "ELi1EEEvNS" in name else 50 if "ELi2EEEvNS" in name else 68
+        assert sum("v_mfma" in l for l in body) >= need, name
 
 
 def _loop_depths(body):
@@ -122,8 +125,8 @@ def test_checker_accepts_compiler_scheduled_mfma(tmp_path):
 
 
 def test_checker_finds_planted_hazards(decode_bodies):
-    # the fp8, page-size-16 kernel (whose fences guard reads the checker must see)
-    body = next(b for n, b in decode_bodies.items() if "ILb1ELi16ELb0E" in n)
+    # the fp8 sparse kernel (whose fences guard reads the checker must see)
+    body = next(b for n, b in decode_bodies.items() if "ILb1ELi0ELi0E" in n)
     assert not ih.check_body(body)
     # a read of an MFMA result right after the MFMA
     i = next(k for k, l in enumerate(body) if "v_mfma" in l)
@@ -150,7 +153,7 @@ def test_checker_knows_the_longer_fp8_mfma_window(decode_bodies):
     """The fp8 query kernels' v_mfma_f32_32x32x64_f8f6f4 needs 20 wait states
     before its result is read: the kernels pass, and a read after only the 12
     that suffice for the bf16 MFMA is flagged."""
-    body = next(b for n, b in decode_bodies.items() if "ILb1ELi64ELb1E" in n)
+    body = next(b for n, b in decode_bodies.items() if "ILb1ELi64ELi1E" in n)
     assert not ih.check_body(body)
     i = next(k for k, l in enumerate(body) if "v_mfma_f32_32x32x64_f8f6f4" in l)
     dst = body[i].split()[1].rstrip(",")
