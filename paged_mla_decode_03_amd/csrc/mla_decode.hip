@@ -1510,7 +1510,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   // One round trip before any arithmetic: the O rows of the first MB segments
   // and the (max, sum) of the first 64 (one per lane) are all in flight
   // together; lane l holds dims 8l .. 8l + 8 of each O row.
-  constexpr int MB = 8;  // O rows in flight (65 VGPRs: 7 waves per SIMD)
+  constexpr int MB = 7;  // O rows in flight (61 VGPRs: 8 waves per SIMD, all a SIMD holds)
   // a sink is one more softmax term with no value row: it joins the max and
   // the denominator
   const float sink = (p.sinks != nullptr) ? p.sinks[head] * LOG2E : -INFINITY;
