@@ -264,8 +264,8 @@ void mla_decode_internal_set_grid_override(int32_t grid);
  * workgroup an equal share of (tiles + segment starts x cost), where a segment
  * is one workgroup's contiguous run of 32-row KV tiles of one 128-pair unit and
  * its start (query load, first tiles in flight, partial-output store) is
- * charged `tiles` tile-equivalents.  Negative restores the default (8); values
- * are capped at 256.  Changes how KV ranges are split and merged, never the
+ * charged `tiles` tile-equivalents.  Negative restores the defaults (8; 4 in
+ * the sparse top-k layout); values are capped at 256.  Changes how KV ranges are split and merged, never the
  * result beyond rounding.  Affects later calls on every device; not thread-safe
  * against concurrent launches.
  */

@@ -92,8 +92,12 @@ constexpr float LN2 = 0.6931471805599453f;
 // reference by more than 2^32: P and the fp32 sums stay far from overflow below.
 constexpr float RESCALE_THRESHOLD = 32.0f;
 // Work-split cost of a segment's start (query load, first tiles, O store) in
-// tile-equivalents; the split balances tiles plus this per segment.
+// tile-equivalents; the split balances tiles plus this per segment.  The
+// sparse layout's units are short (a list of K entries), and there a lower
+// charge, i.e. more workgroups per unit, measured faster (65.3 against 67.5 us
+// for 64 rows x 2048 entries; 2 and 12 were slower).
 constexpr int SEG_COST_DEFAULT = 8;
+constexpr int SEG_COST_SPARSE = 4;
 constexpr int SEG_COST_MAX = 256;
 
 static_assert(LDS_BYTES <= 163840, "LDS budget");
@@ -1647,7 +1651,7 @@ __global__ void fp8_to_bf16_kernel(const u32x2* in, bf16x8* out, int64_t n) {
 constexpr int MAX_DEVICES = 64;
 std::atomic<int> g_cu_count[MAX_DEVICES];
 std::atomic<int> g_grid_override{0};
-std::atomic<int> g_seg_cost{SEG_COST_DEFAULT};
+std::atomic<int> g_seg_cost{-1};  // negative: the layout's default
 std::atomic<void*> g_ev_start{nullptr};
 std::atomic<void*> g_ev_stop{nullptr};
 
@@ -1832,7 +1836,8 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   p.scale_log2 = bmm1_scale * LOG2E;
   p.bmm2 = bmm2_scale;
   p.causal = causal ? 1 : 0;
-  p.seg_cost = g_seg_cost.load(std::memory_order_relaxed);
+  const int seg_cost = g_seg_cost.load(std::memory_order_relaxed);
+  p.seg_cost = seg_cost >= 0 ? seg_cost : (sparse ? SEG_COST_SPARSE : SEG_COST_DEFAULT);
   p.bmm1_dev = opts ? opts->bmm1_scale : nullptr;
   p.bmm2_dev = opts ? opts->bmm2_scale : nullptr;
   // a sink is one softmax term per (row, head): in a sequence-sharded decode
@@ -1896,7 +1901,7 @@ int mla_merge_partials(const void* outs, const float* lses, int32_t num_partials
 void mla_decode_internal_set_grid_override(int32_t grid) { g_grid_override.store(grid > 0 ? grid : 0); }
 
 void mla_decode_internal_set_segment_cost(int32_t tiles) {
-  g_seg_cost.store(tiles < 0 ? SEG_COST_DEFAULT : std::min(tiles, SEG_COST_MAX));
+  g_seg_cost.store(tiles < 0 ? -1 : std::min(tiles, SEG_COST_MAX));
 }
 
 void mla_decode_internal_set_kernel_events(void* start_event, void* stop_event) {
