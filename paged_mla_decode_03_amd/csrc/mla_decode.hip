@@ -941,6 +941,9 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     else wait_vmcnt<2 * PER_TILE>();
   };
 
+  // the fast path needs logits increasing with the raw scores; c has the
+  // sign of bmm1 in every lane (split mode keeps it from underflowing), so
+  // this test is wave-uniform
   const bool c_pos = c > 0.f;
 
   // ---------------- softmax (exp2 domain) of one tile's scores s; value k is
@@ -1217,6 +1220,10 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
       amax = max_halves(amax);
       const int e = 8 - __builtin_amdgcn_frexp_expf(amax);
       c = __builtin_amdgcn_ldexpf(p.scale_log2, -e);
+      // a positive scale stays positive in every lane (the fast-path test
+      // must agree across the wave): at worst the smallest normal float, where
+      // the logits are below 2^-100 and were smaller still
+      if (p.scale_log2 > 0.f) c = fmaxf(c, 1.17549435e-38f);
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         i32x8 hi8, lo8;

@@ -78,3 +78,16 @@ def test_zero_rows_and_single_spikes():
     q[r, h, rng.integers(0, D, r.size)] = rng.choice([-6.0, 5.0], r.size)
     w.q_bits = to_bf16_bits(q)
     compare_with_oracle(w)
+
+
+def test_tiny_scale_with_tiny_pairs():
+    """bmm1 = 1e-30 and pairs scaled by 2^-120: the lane's logit scale
+    bmm1 log2(e) 2^-e would underflow to zero in float32; it is held at the
+    smallest normal float so that every lane of a wave takes the same softmax
+    path.  The logits are all ~0: uniform weights, as in the oracle."""
+    w = _workload("split_tiny", 96, bmm1_scale=1e-30)
+    rng = np.random.default_rng(97)
+    q = _bf16_values(w.q_bits)
+    q = q * np.exp2(rng.choice(np.array([-120.0, -118.0, 0.0]), size=q.shape[:2]))[..., None]
+    w.q_bits = to_bf16_bits(q)
+    compare_with_oracle(w)
