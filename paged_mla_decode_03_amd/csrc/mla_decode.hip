@@ -37,9 +37,12 @@
 //     logits are taken relative to a per-pair reference max fixed by the first
 //     visible tile; a logit beyond it by more than 2^32 restarts the segment with
 //     the observed max (never happens for sane inputs; keeps O free of rescales).
-//   * fp8 E4M3FN KV is converted exactly to bf16 in registers (v_cvt_pk_f32_fp8),
-//     so the MFMA path is the same and scales only enter through bmm1/bmm2.  With
-//     an fp8 query as well, QK^T runs on v_mfma_f32_32x32x64_f8f6f4 instead.
+//   * fp8 E4M3FN KV: QK^T runs on v_mfma_f32_32x32x64_f8f6f4 straight from the
+//     landed fp8 tile, with an fp8 query as given or with a bf16 query split per
+//     (row, head) into two E4M3 terms under a power-of-two scale (18 MFMAs per
+//     tile, exact within 2^9 of the pair's largest element).  V fragments are
+//     widened exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8) for the bf16 P.V, as
+//     are the rows of the sparse gather.  Scales only enter through bmm1/bmm2.
 //   * Options (mla_decode_paged_ex): device-resident scales, per-head attention
 //     sinks (one more softmax term, applied in the merge), a sequence-sharded
 //     partial mode (causal limits from global lengths), and a sparse top-k
