@@ -1,20 +1,29 @@
 """Throughput benchmark: batched paged MLA decode on one MI355X.
 
-One step = one mla_decode_paged call (device work plan + decode kernel +
-split merge) over the whole batch of the DeepSeek-V3-shaped bf16 decode
-workload (B=64, H=128, q_len=1, 576/512 dims, seq_lens uniform in
-[1024, 8192], page size 64, shuffled pages), inputs resident in HBM.
+One step = one mla_decode_paged call (the whole launch: device work plan,
+decode and split merge) over the whole batch of a workload, inputs resident
+in HBM.  The headline workload is the DeepSeek-V3-shaped bf16 decode (B=64,
+H=128, q_len=1, 576/512 dims, seq_lens uniform in [1024, 8192], page size 64,
+shuffled pages).
 
-Prints one JSON line with the metric (KV-tokens/s), TFLOP/s, algorithmic
-GB/s, the decode kernel's roofline fraction (timed with HIP events on the
-launch stream) and the float64 CPU oracle's throughput on a bounded sample of
-the same workload.
+By default every one of the five configured workloads (tiny bf16, the
+headline, uniform spec 1+3 causal, ragged packed causal, long-context fp8 KV)
+is timed in turn, each with its own warmup and timed steps, the headline
+last; the one JSON line carries the headline's figures and, under "configs",
+each workload's.  Per workload: KV-tokens/s, TFLOP/s and algorithmic GB/s
+over the timed steps, and the roofline fraction of the launch (algorithmic
+bytes or flops over the mean device time from the first kernel's start to the
+last kernel's end, HIP events on the launch stream), plus the decode kernel's
+own fraction.  The float64 CPU oracle is timed on a bounded sample of the
+headline workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
                   [--no-cpu-baseline] [--all]
 
-NAME is one of the paged workloads (paged_mla_decode_03_amd.inputs.WORKLOADS)
-or the sparse top-k workload sparse_topk_decode (SPARSE_WORKLOADS).
+--workload NAME times that workload alone (a paged workload of
+paged_mla_decode_03_amd.inputs.WORKLOADS, the fp8-query one of Q8_WORKLOADS or
+the sparse top-k one of SPARSE_WORKLOADS); --all adds the fp8-query and sparse
+workloads to the default run.
 """
 
 import argparse
@@ -76,17 +85,19 @@ def kernel_source_sha256():
 
 
 def profiled_traffic(workload):
-    """HBM bytes per decode-kernel launch from a committed rocprofv3 summary, or
-    None when no summary matches both the workload and the current kernel source.
+    """HBM bytes per launch (every kernel of one call) from the committed
+    rocprofv3 summaries, or None when none matches both the workload and the
+    current kernel source.
 
-    A summary carries one line
-      bench-traffic: workload=W kernel_sha256=H fetch_kib=F write_kib=X fetch_scale=a write_scale=b
+    A summary carries one line per kernel of the launch
+      bench-traffic: workload=W kernel=K kernel_sha256=H fetch_kib=F write_kib=X fetch_scale=a write_scale=b
     where F and X are the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch)
     and a, b the factors that turn them into bytes for a plain copy of known size.
     """
     if not os.path.isdir(PROFILES):
         return None
     sha = kernel_source_sha256()
+    total, seen = 0.0, set()
     for name in sorted(os.listdir(PROFILES)):
         if not name.endswith((".md", ".txt")):
             continue
@@ -96,16 +107,19 @@ def profiled_traffic(workload):
                 if not line.startswith("bench-traffic:"):
                     continue
                 kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
-                if kv.get("workload") == workload and kv.get("kernel_sha256") == sha:
-                    return int((float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
-                                float(kv["write_kib"]) * float(kv["write_scale"])) * 1024)
-    return None
+                key = kv.get("kernel", "decode")
+                if kv.get("workload") == workload and kv.get("kernel_sha256") == sha and key not in seen:
+                    seen.add(key)
+                    total += (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                              float(kv["write_kib"]) * float(kv["write_scale"])) * 1024
+    return int(total) if seen else None
 
 
 def time_steps(step, steps, warmup):
     """Run warmup untimed steps, then time exactly `steps` steps (bracketed by
-    device synchronisation) with the library's decode-kernel events recorded
-    on the launch stream.  Returns (ms per step, mean decode-kernel ms)."""
+    device synchronisation), the library recording HIP events on the launch
+    stream before its first kernel, after the decode kernel and after its
+    last kernel.  Returns (ms per step, mean launch ms, mean decode-kernel ms)."""
     import numpy as np
     import torch
     from paged_mla_decode_03_amd import binding
@@ -113,26 +127,29 @@ def time_steps(step, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        b.record()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for trio in ev:
+        for e in trio:
+            e.record()
     torch.cuda.synchronize()
     log(f"[bench] timing {steps} steps")
     t0 = time.perf_counter()
     for i in range(steps):
-        binding.set_kernel_events(ev[i][0], ev[i][1])
+        binding.set_kernel_events(ev[i][0], ev[i][2], ev[i][1])
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     binding.set_kernel_events(None, None)
-    return (t1 - t0) * 1e3 / steps, float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch = float(np.mean([a.elapsed_time(c) for a, b, c in ev]))
+    decode = float(np.mean([a.elapsed_time(b) for a, b, c in ev]))
+    return (t1 - t0) * 1e3 / steps, launch, decode
 
 
 def roofline(counts, kern_ms, name, q8=False):
-    """The decode kernel against its bound: HBM if its algorithmic bytes take
-    longer at peak than its algorithmic flops at the MFMA peak (bf16; with an
-    fp8 query, QK^T at the fp8 peak and P.V at the bf16 one)."""
+    """A launch (or one kernel of it) timed at kern_ms against its bound: HBM
+    if its algorithmic bytes take longer at peak than its algorithmic flops at
+    the MFMA peak (bf16; with an fp8 query, QK^T at the fp8 peak and P.V at the
+    bf16 one)."""
     from paged_mla_decode_03_amd.metrics import PEAK_HBM_GBS, PEAK_MFMA_TFLOPS, mixed_mfma_peak
     peak_mfma = mixed_mfma_peak() if q8 else PEAK_MFMA_TFLOPS["bf16"]
     t_hbm = counts["bytes"] / (PEAK_HBM_GBS * 1e9)
@@ -173,6 +190,43 @@ def sparse_cpu_baseline(w, lists, budget_s=10.0):
                       f"in {dt:.1f} s, float64 NumPy"}
 
 
+def _result(name, counts, ms_step, launch_ms, decode_ms, steps, warmup, dtype, data, config, q8=False):
+    roof = roofline(counts, launch_ms, name, q8=q8)
+    dec = roofline(counts, decode_ms, name, q8=q8)
+    return {
+        "metric": METRIC,
+        "value": counts["kv_tokens"] / (ms_step * 1e-3),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": data,
+        "config": config,
+        "tflops": counts["flops"] / (ms_step * 1e-3) / 1e12,
+        "gbps": counts["bytes"] / (ms_step * 1e-3) / 1e9,
+        "launch_ms": launch_ms,
+        "decode_kernel_ms": decode_ms,
+        "decode_kernel_frac": dec["frac"],
+        "kernel_source_sha256": kernel_source_sha256(),
+        "roofline": roof,
+    }
+
+
+def _dtype_label(kv_dtype, q8):
+    """The arithmetic each path computes in."""
+    if kv_dtype == "bf16":
+        return "bf16"
+    if q8:
+        return "fp8 e4m3 KV and query: QK^T on fp8 MFMA, P.V on bf16 MFMA"
+    return ("fp8 e4m3 KV, bf16 query: QK^T on fp8 MFMA (query split into two e4m3 terms), "
+            "P.V on bf16 MFMA (V widened exactly)")
+
+
 def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
     """One step = one sparse top-k decode call over the whole batch."""
     import torch
@@ -209,30 +263,15 @@ def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
-    ms_step, kern_ms = time_steps(step, steps, warmup)
-    res = {
-        "metric": METRIC,
-        "value": counts["kv_tokens"] / (ms_step * 1e-3),
-        "unit": "KV-tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma",
-        "data": f"synthetic (seeded N(0,1) q/kv, shuffled pages, seeded top-k selections of each request; "
-                f"{max(1, rotate)} cache copies rotated across steps)",
-        "config": {"workload": name, "rows": w.total_q, "heads": w.num_heads, "top_k": K,
-                   "seq_lens": list(spec["seq_len_range"]), "page_size": w.page_size, "kv_dtype": w.kv_dtype,
-                   "lse": w.want_lse, "kv_tokens": counts["kv_tokens"]},
-        "tflops": counts["flops"] / (ms_step * 1e-3) / 1e12,
-        "gbps": counts["bytes"] / (ms_step * 1e-3) / 1e9,
-        "decode_kernel_ms": kern_ms,
-        "kernel_source_sha256": kernel_source_sha256(),
-        "roofline": roofline(counts, kern_ms, name),
-    }
+    ms_step, launch_ms, decode_ms = time_steps(step, steps, warmup)
+    config = {"workload": name, "rows": w.total_q, "heads": w.num_heads, "top_k": K,
+              "seq_lens": list(spec["seq_len_range"]), "page_size": w.page_size, "kv_dtype": w.kv_dtype,
+              "lse": w.want_lse, "kv_tokens": counts["kv_tokens"]}
+    data = (f"synthetic (seeded N(0,1) q/kv, shuffled pages, seeded top-k selections of each request; "
+            f"{max(1, rotate)} cache copies rotated across steps)")
+    res = _result(name, counts, ms_step, launch_ms, decode_ms, steps, warmup,
+                  "bf16" if w.kv_dtype == "bf16" else "fp8 e4m3 KV widened exactly to bf16, bf16 MFMA",
+                  data, config)
     if want_cpu:
         log("[bench] cpu baseline (oracle)")
         res["cpu_baseline"] = sparse_cpu_baseline(w, lists)
@@ -287,43 +326,31 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
-    ms_step, kern_ms = time_steps(step, steps, warmup)
-    kv_bytes_per = 2 if w.kv_dtype == "bf16" else 1
-    dtype = "bf16" if w.kv_dtype == "bf16" else "fp8-kv/bf16-mfma"
-    roof = roofline(counts, kern_ms, name, q8=q8)
-    if q8:
-        dtype = "fp8 QK^T / bf16 P.V"
+    ms_step, launch_ms, decode_ms = time_steps(step, steps, warmup)
     spec = WORKLOADS[base]
-    res = {
-        "metric": METRIC,
-        "value": counts["kv_tokens"] / (ms_step * 1e-3),
-        "unit": "KV-tokens/s",
-        "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if kv_bytes_per == 2 else dtype,
-        "data": f"synthetic (seeded N(0,1) q/kv, shuffled pages; {max(1, rotate)} cache copies rotated across steps)"
-                + ("; query rounded to fp8 E4M3FN, q_scale 1" if q8 else ""),
-        "config": {"workload": name, "batch": B, "heads": H, **({"q_dtype": "fp8_e4m3fn"} if q8 else {}),
-                   "q_len": spec.get("q_len") if "q_len_range" not in spec else list(spec["q_len_range"]),
-                   "seq_lens": list(spec["seq_len_range"]) if "seq_len_range" in spec else
-                   (list(spec["seq_len_loguniform"]) if "seq_len_loguniform" in spec else spec.get("seq_lens")),
-                   "page_size": w.page_size, "kv_dtype": w.kv_dtype, "causal": w.causal, "lse": w.want_lse,
-                   "kv_tokens": counts["kv_tokens"]},
-        "tflops": counts["flops"] / (ms_step * 1e-3) / 1e12,
-        "gbps": counts["bytes"] / (ms_step * 1e-3) / 1e9,
-        "decode_kernel_ms": kern_ms,
-        "kernel_source_sha256": kernel_source_sha256(),
-        "roofline": roof,
-    }
+    config = {"workload": name, "batch": B, "heads": H, **({"q_dtype": "fp8_e4m3fn"} if q8 else {}),
+              "q_len": spec.get("q_len") if "q_len_range" not in spec else list(spec["q_len_range"]),
+              "seq_lens": list(spec["seq_len_range"]) if "seq_len_range" in spec else
+              (list(spec["seq_len_loguniform"]) if "seq_len_loguniform" in spec else spec.get("seq_lens")),
+              "page_size": w.page_size, "kv_dtype": w.kv_dtype, "causal": w.causal, "lse": w.want_lse,
+              "kv_tokens": counts["kv_tokens"]}
+    data = (f"synthetic (seeded N(0,1) q/kv, shuffled pages; {max(1, rotate)} cache copies rotated across steps)"
+            + ("; query rounded to fp8 E4M3FN, q_scale 1" if q8 else ""))
+    res = _result(name, counts, ms_step, launch_ms, decode_ms, steps, warmup, _dtype_label(w.kv_dtype, q8), data,
+                  config, q8=q8)
     if want_cpu:
         log("[bench] cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, q_codes=fp8_query_codes(w) if q8 else None)
     return res
+
+
+def _summary(r):
+    """The per-workload figures carried under "configs" of the JSON line."""
+    keep = ("value", "unit", "ms_per_step", "launch_ms", "decode_kernel_ms", "decode_kernel_frac", "tflops", "gbps",
+            "dtype", "roofline")
+    d = {k: r[k] for k in keep}
+    d["kv_tokens"] = r["config"]["kv_tokens"]
+    return d
 
 
 def main():
@@ -332,12 +359,12 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps first: the GPU reaches steady clocks only after tens of ms of work")
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None, help="time this workload alone")
     ap.add_argument("--rotate", type=int, default=3,
                     help="copies of the KV cache and Q read in turn by consecutive steps (1 = one copy, which "
                          "can sit in the 256 MB MALL for the smaller workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--all", action="store_true", help="also time the other workloads (lines on stderr)")
+    ap.add_argument("--all", action="store_true", help="also time the fp8-query and sparse top-k workloads")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed steps, run 3 plain device-to-device copies of this many bytes "
                          "(HBM-counter calibration under rocprofv3 --pmc)")
@@ -356,12 +383,30 @@ def main():
         fn = run_sparse_workload if name in SPARSE_WORKLOADS else run_workload
         return fn(name, args.steps, args.warmup, want_cpu, args.rotate)
 
-    res = run(args.workload, not args.no_cpu_baseline)
-    if args.all:
-        for name in WORKLOAD_ORDER + list(SPARSE_WORKLOADS) + list(Q8_WORKLOADS):
-            if name == args.workload:
-                continue
-            log("[bench-extra] " + json.dumps(run(name, False)))
+    if args.workload is not None:
+        res = run(args.workload, not args.no_cpu_baseline)
+        log("[bench] " + json.dumps(_summary(res)))
+    else:
+        # the five configured workloads, the headline last
+        order = [n for n in WORKLOAD_ORDER if n != DEFAULT_WORKLOAD] + [DEFAULT_WORKLOAD]
+        configs = {}
+        for name in order:
+            r = run(name, False)
+            configs[name] = _summary(r)
+            log(f"[bench] {name}: " + json.dumps(configs[name]))
+        res = r
+        extra = {}
+        if args.all:
+            for name in list(Q8_WORKLOADS) + list(SPARSE_WORKLOADS):
+                extra[name] = _summary(run(name, False))
+                log(f"[bench] {name}: " + json.dumps(extra[name]))
+        res["configs"] = configs
+        if extra:
+            res["extra_workloads"] = extra
+        if not args.no_cpu_baseline:
+            from paged_mla_decode_03_amd.inputs import named_workload
+            log("[bench] cpu baseline (oracle)")
+            res["cpu_baseline"] = cpu_baseline(named_workload(DEFAULT_WORKLOAD, poison=False))
     if args.copy_bytes > 0:
         n = (args.copy_bytes + 15) // 16 * 16
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

@@ -272,13 +272,15 @@ void mla_decode_internal_set_grid_override(int32_t grid);
 void mla_decode_internal_set_segment_cost(int32_t tiles);
 
 /*
- * Measurement hook, not part of the serving interface: when both are non-NULL,
- * later mla_decode_paged calls record start_event (a hipEvent_t) on their stream
- * right before the decode kernel and stop_event right after it, before the split
- * merge, so a caller can time the decode kernel alone.  NULL, NULL turns it off.
- * The events stay owned by the caller.
+ * Measurement hook, not part of the serving interface: when start_event and
+ * stop_event are non-NULL, later mla_decode_paged calls record start_event (a
+ * hipEvent_t) on their stream right before their first kernel and stop_event
+ * right after their last one, so a caller can time the whole launch on the
+ * stream it runs on; decode_event, if non-NULL, is recorded right after the
+ * decode kernel (before a separate split merge, where there is one).  NULL
+ * start or stop turns it off.  The events stay owned by the caller.
  */
-void mla_decode_internal_set_kernel_events(void* start_event, void* stop_event);
+void mla_decode_internal_set_kernel_events(void* start_event, void* decode_event, void* stop_event);
 
 /*
  * Test hook, not part of the serving interface: widen n_groups x 8 fp8 E4M3FN

@@ -87,7 +87,7 @@ def load_library():
     lib.mla_decode_internal_set_grid_override.restype = None
     lib.mla_decode_internal_set_segment_cost.argtypes = [i32]
     lib.mla_decode_internal_set_segment_cost.restype = None
-    lib.mla_decode_internal_set_kernel_events.argtypes = [vp, vp]
+    lib.mla_decode_internal_set_kernel_events.argtypes = [vp, vp, vp]
     lib.mla_decode_internal_set_kernel_events.restype = None
     lib.mla_decode_internal_fp8_to_bf16.argtypes = [vp, vp, i64, vp]
     lib.mla_decode_internal_fp8_to_bf16.restype = ctypes.c_int
@@ -159,14 +159,20 @@ def set_segment_cost(tiles):
     load_library().mla_decode_internal_set_segment_cost(int(tiles))
 
 
-def set_kernel_events(start_event, stop_event):
-    """Measurement hook: record two torch.cuda.Event (HIP events) around the
-    decode kernel of every later call; (None, None) turns it off."""
+def set_kernel_events(start_event, stop_event, decode_event=None):
+    """Measurement hook: record torch.cuda.Event (HIP events) on the launch
+    stream of every later call: start_event before its first kernel,
+    stop_event after its last, decode_event (optional) right after the decode
+    kernel.  set_kernel_events(None, None) turns it off.  torch only counts an
+    event as recorded once torch itself has recorded it, so record each event
+    once through torch before handing it over."""
     lib = load_library()
     if start_event is None or stop_event is None:
-        lib.mla_decode_internal_set_kernel_events(None, None)
+        lib.mla_decode_internal_set_kernel_events(None, None, None)
     else:
-        lib.mla_decode_internal_set_kernel_events(start_event.cuda_event, stop_event.cuda_event)
+        lib.mla_decode_internal_set_kernel_events(start_event.cuda_event,
+                                                  None if decode_event is None else decode_event.cuda_event,
+                                                  stop_event.cuda_event)
 
 
 def fp8_to_bf16_device(codes):
@@ -196,7 +202,16 @@ def dims_for(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len_q):
         kv_cache = kv_cache.squeeze(1)
     if kv_cache.dim() != 3 or kv_cache.shape[-1] != D_QK:
         raise ValueError("kv_cache must be [pages, page_size, 576]")
+    if query.shape[-1] != D_QK:
+        raise ValueError(f"query rows must be {D_QK} wide (512 latent + 64 RoPE), got {query.shape[-1]}")
+    if seq_lens.dim() != 1:
+        raise ValueError("seq_lens must be 1-D [B]")
     B = int(seq_lens.shape[0])
+    if block_tables.dim() != 2 or int(block_tables.shape[0]) != B:
+        raise ValueError(f"block_tables must be 2-D [B={B}, W]")
+    if qo_indptr is not None and (qo_indptr.dim() != 1 or int(qo_indptr.shape[0]) != B + 1
+                                  or not qo_indptr.is_contiguous()):
+        raise ValueError(f"qo_indptr must be a contiguous 1-D tensor of B+1={B + 1} offsets")
     if qo_indptr is None:
         if query.dim() != 4 or query.shape[0] != B:
             raise ValueError("fixed launch needs query [B, SQ, H, 576]")
@@ -263,6 +278,10 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
         raise TypeError("block_tables and seq_lens must be int32")
     if qo_indptr is not None and (qo_indptr.dtype != torch.int32 or not qo_indptr.is_cuda):
         raise TypeError("qo_indptr must be an int32 device tensor")
+    for name, t in (("kv_cache", kv_cache), ("workspace_buffer", workspace_buffer), ("block_tables", block_tables),
+                    ("seq_lens", seq_lens), ("qo_indptr", qo_indptr)):
+        if t is not None and t.device != query.device:
+            raise ValueError(f"{name} must be on the query's device {query.device}")
     dims, max_q, total_q, H = dims_for(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len_q)
     out_shape = tuple(query.shape[:-1]) + (KV_LORA_RANK,)
     if out is None:
@@ -281,12 +300,14 @@ def decode(query, kv_cache, workspace_buffer, block_tables, seq_lens, max_seq_le
     b1 = _device_scalar("bmm1_scale", bmm1_scale, query.device)
     b2 = _device_scalar("bmm2_scale", bmm2_scale, query.device)
     if sinks is not None and (sinks.dtype != torch.float32 or tuple(sinks.shape) != (H,) or not sinks.is_cuda
-                              or not sinks.is_contiguous()):
-        raise TypeError(f"sinks must be a contiguous float32 device tensor of shape ({H},)")
+                              or not sinks.is_contiguous() or sinks.device != query.device):
+        raise TypeError(f"sinks must be a contiguous float32 tensor of shape ({H},) on the query's device")
     if dcp is not None:
         lens_g, cp_world, cp_rank = dcp
-        if lens_g.dtype != torch.int32 or not lens_g.is_cuda or tuple(lens_g.shape) != tuple(seq_lens.shape):
-            raise TypeError("dcp seq_lens_global must be an int32 device tensor shaped like seq_lens")
+        if (lens_g.dtype != torch.int32 or not lens_g.is_cuda or tuple(lens_g.shape) != tuple(seq_lens.shape)
+                or not lens_g.is_contiguous() or lens_g.device != query.device):
+            raise TypeError("dcp seq_lens_global must be a contiguous int32 tensor shaped like seq_lens on the "
+                            "query's device")
         if not return_lse:
             raise ValueError("the sequence-sharded mode needs return_lse=True")
     if b1 is None and b2 is None and sinks is None and dcp is None and not q8:
@@ -367,8 +388,11 @@ def decode_sparse(query, kv_cache, workspace_buffer, indices, *, top_k=None, out
     b1 = _device_scalar("bmm1_scale", bmm1_scale, query.device)
     b2 = _device_scalar("bmm2_scale", bmm2_scale, query.device)
     if sinks is not None and (sinks.dtype != torch.float32 or tuple(sinks.shape) != (H,) or not sinks.is_cuda
-                              or not sinks.is_contiguous()):
-        raise TypeError(f"sinks must be a contiguous float32 device tensor of shape ({H},)")
+                              or not sinks.is_contiguous() or sinks.device != query.device):
+        raise TypeError(f"sinks must be a contiguous float32 tensor of shape ({H},) on the query's device")
+    for name, t in (("kv_cache", kv_cache), ("workspace_buffer", workspace_buffer), ("indices", indices)):
+        if t.device != query.device:
+            raise ValueError(f"{name} must be on the query's device {query.device}")
     opts = MlaOptions(_ptr(b1), _ptr(b2), _ptr(sinks), None, 1, 0, k)
     ws_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
     rc = mla_decode_paged_ex(query, kv_cache, indices, None, None, 1, 1, 1.0 if b1 is not None else bmm1_scale,

@@ -1663,6 +1663,7 @@ std::atomic<int> g_cu_count[MAX_DEVICES];
 std::atomic<int> g_grid_override{0};
 std::atomic<int> g_seg_cost{-1};  // negative: the layout's default
 std::atomic<void*> g_ev_start{nullptr};
+std::atomic<void*> g_ev_decode{nullptr};
 std::atomic<void*> g_ev_stop{nullptr};
 
 int device_grid(int* grid_out) {
@@ -1870,8 +1871,9 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   hipStream_t s = (hipStream_t)stream;
   const bool fp8 = dims->kv_dtype == MLA_KV_FP8_E4M3FN;
   void* ev0 = g_ev_start.load(std::memory_order_relaxed);
+  void* evd = g_ev_decode.load(std::memory_order_relaxed);
   void* ev1 = g_ev_stop.load(std::memory_order_relaxed);
-  if (ev0 != nullptr) (void)hipEventRecord((hipEvent_t)ev0, s);
+  if (ev0 != nullptr && ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev0, s);
   // fp8 cache: an fp8 query runs as given (mode 1), a bf16 query as two fp8
   // terms (mode 2); the sparse gather keeps the widened bf16 path (mode 0)
   if (sparse) {
@@ -1888,9 +1890,10 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
     case 32: launch_decode<false, 32, 0>(p, s); break;
     default: launch_decode<false, 64, 0>(p, s); break;
   }
-  if (ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev1, s);
+  if (ev0 != nullptr && ev1 != nullptr && evd != nullptr) (void)hipEventRecord((hipEvent_t)evd, s);
   const int items = dims->total_q * dims->num_heads;
   hipLaunchKernelGGL(mla_merge_kernel, dim3((items + 3) / 4), dim3(MERGE_THREADS), 0, s, p);
+  if (ev0 != nullptr && ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev1, s);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -1914,8 +1917,9 @@ void mla_decode_internal_set_segment_cost(int32_t tiles) {
   g_seg_cost.store(tiles < 0 ? -1 : std::min(tiles, SEG_COST_MAX));
 }
 
-void mla_decode_internal_set_kernel_events(void* start_event, void* stop_event) {
+void mla_decode_internal_set_kernel_events(void* start_event, void* decode_event, void* stop_event) {
   g_ev_start.store(start_event);
+  g_ev_decode.store(decode_event);
   g_ev_stop.store(stop_event);
 }
 

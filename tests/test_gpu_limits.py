@@ -26,10 +26,10 @@ def _default_grid():
 
 
 def test_largest_batch():
-    """1024 requests (four per plan thread), short ragged lengths, sampled."""
+    """1024 requests (four per plan thread), short ragged lengths, every request."""
     w = make_workload("maxb", seed=90, batch=MAX_BATCH, seq_len_range=(1, 40), num_heads=16, q_len=1, page_size=16,
                       bmm1_scale=INV_SQRT_192, causal=True, want_lse=True)
-    compare_with_oracle(w, requests=[0, 1, 255, 256, 511, 700, 1022, 1023])
+    compare_with_oracle(w)
 
 
 def test_every_request_one_row():

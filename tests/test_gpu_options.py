@@ -117,3 +117,70 @@ def test_graph_replays_follow_device_scales():
         ref_o, ref_l = _run(w, t, q, max_q, ws, bmm1_scale=float(np.float32(s1)), bmm2_scale=float(np.float32(s2)),
                             sinks=sinks)
         assert torch.equal(got_o, ref_o.view_as(got_o)) and torch.equal(got_l, ref_l.view_as(got_l)), (s1, s2)
+
+
+def _compositions(rng, B, total, lo, hi, lens, n):
+    """n distinct per-request query-length vectors (each in [lo, hi], at most the
+    request's length) with the same sum `total`."""
+    out = []
+    while len(out) < n:
+        q = rng.integers(lo, hi, endpoint=True, size=B)
+        q = np.minimum(q, lens)
+        d = total - int(q.sum())
+        # move the difference onto requests that have room, one row at a time
+        order = rng.permutation(B)
+        for b in np.concatenate([order] * (hi * B)):
+            if d == 0:
+                break
+            if d > 0 and q[b] < min(hi, lens[b]):
+                q[b] += 1
+                d -= 1
+            elif d < 0 and q[b] > lo:
+                q[b] -= 1
+                d += 1
+        if d == 0 and not any(np.array_equal(q, o) for o in out):
+            out.append(q.copy())
+    return [np.concatenate([[0], np.cumsum(q)]).astype(np.int32) for q in out]
+
+
+def test_graph_replays_follow_qo_indptr_updates():
+    """A packed launch captured once: between replays, eager work rewrites the
+    values of qo_indptr in its stable storage (same total_q and max_q_len, every
+    offset vector valid), as the FlashInfer API docs contract paragraph allows.
+    Each of 24 replays must equal, bitwise, an eager decode with the same
+    offsets, and match the oracle."""
+    w = make_workload("gqo", seed=45, batch=7, seq_len_range=(40, 1200), num_heads=32, q_len_range=(1, 6),
+                      page_size=32, bmm1_scale=INV_SQRT_192, causal=True, want_lse=True)
+    H, R = w.num_heads, w.total_q
+    rng = np.random.default_rng(46)
+    variants = _compositions(rng, w.batch, R, 1, w.max_q_len, w.seq_lens.astype(np.int64), 6)
+    t, q, max_q, ws = _setup(w)
+    qo = t["qo_indptr"]
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    kw = dict(qo_indptr=qo, max_seq_len_q=max_q, return_lse=True, causal=True, out=out, lse=lse,
+              bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale)
+    binding.decode(q, t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.decode(q, t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, **kw)
+    eager_out = torch.empty_like(out)
+    eager_lse = torch.empty_like(lse)
+    for i in range(24):
+        v = variants[i % len(variants)]
+        qo.copy_(torch.from_numpy(v))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        binding.decode(q, t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, qo_indptr=qo,
+                       max_seq_len_q=max_q, return_lse=True, causal=True, out=eager_out, lse=eager_lse,
+                       bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, eager_out) and torch.equal(got_l, eager_lse), f"replay {i}"
+        if i < len(variants):
+            prob = dataclasses.replace(oracle.MlaProblem(**w.oracle_problem_kwargs()), qo_indptr=v)
+            ref_o, ref_l = oracle.reference_decode(prob)
+            check_close(got_o.float().cpu().numpy(), ref_o, f"replay {i} out")
+            check_close(got_l.cpu().numpy(), ref_l, f"replay {i} lse")

@@ -13,7 +13,7 @@ import torch
 from paged_mla_decode_03_amd import binding
 from paged_mla_decode_03_amd.inputs import make_workload, named_workload, INV_SQRT_192
 
-from gpu_cases import compare_with_oracle, run_hip, sample_requests
+from gpu_cases import compare_with_oracle, run_hip
 
 pytestmark = pytest.mark.gpu
 
@@ -35,13 +35,11 @@ def test_tiny_bf16_full():
 
 @pytest.mark.parametrize("name", ["dsv3_bf16_decode", "spec_1p3_causal", "ragged_packed_causal",
                                   "fp8_long_context"])
-def test_full_size_sampled(name):
-    """Full-size workloads in the benchmark's launch configuration; the oracle
-    checks a sample of requests (shortest, longest, first, last, random)."""
+def test_full_size_all_requests(name):
+    """Full-size workloads in the benchmark's launch configuration, every
+    request of the batch against the oracle."""
     w = named_workload(name)
-    reqs = sample_requests(w, k=2 if name == "fp8_long_context" else 4)
-    print(name, "requests", reqs, flush=True)
-    stats = compare_with_oracle(w, reqs)
+    stats = compare_with_oracle(w)
     print(name, stats, flush=True)
 
 

@@ -48,8 +48,7 @@ def _run_and_check(w, *, inv_q_scale=1.0, sinks=None, what=""):
     ref_o, ref_l = oracle.reference_decode(prob)
     got_o = o.float().reshape(w.total_q, H, 512).cpu().numpy()
     got_l = l.reshape(w.total_q, H).cpu().numpy()
-    rms, _ = check_close(got_o, ref_o, f"{what} out")
-    assert rms < 5e-3, f"{what}: out relative RMS {rms:.2e}"
+    check_close(got_o, ref_o, f"{what} out")
     check_close(got_l, ref_l, f"{what} lse")
 
 
@@ -85,9 +84,10 @@ def test_fp8_query_reference_restart():
     _run_and_check(w, what="restart")
 
 
-def test_full_size_benched_workload_sampled():
+def test_full_size_benched_workload_all_requests():
     """fp8_long_context with an fp8 query at full size (8 requests of 64K-128K
-    rows), in the launch the benchmark times, checked on sampled requests."""
+    rows), in the launch the benchmark times, every request against the
+    oracle."""
     from paged_mla_decode_03_amd.inputs import named_workload, to_device_tensors
     w = named_workload("fp8_long_context", poison=True)
     codes = fp8_query_codes(w)
@@ -101,11 +101,9 @@ def test_full_size_benched_workload_sampled():
     prob = oracle.MlaProblem(**w.oracle_problem_kwargs())
     prob.q_bits = codes
     prob.q_dtype = "fp8_e4m3fn"
-    reqs = [0, int(np.argmax(w.seq_lens)), w.batch - 1]
-    ref_o, ref_l = oracle.reference_decode(prob, requests=reqs)
-    rows = np.concatenate([np.arange(b * 2, b * 2 + 2) for b in reqs])
+    ref_o, ref_l = oracle.reference_decode(prob)
     H = w.num_heads
-    got_o = o.float().reshape(w.total_q, H, 512).cpu().numpy()[rows]
-    got_l = l.reshape(w.total_q, H).cpu().numpy()[rows]
-    check_close(got_o, ref_o[rows], "q8 full-size out")
-    check_close(got_l, ref_l[rows], "q8 full-size lse")
+    got_o = o.float().reshape(w.total_q, H, 512).cpu().numpy()
+    got_l = l.reshape(w.total_q, H).cpu().numpy()
+    check_close(got_o, ref_o, "q8 full-size out")
+    check_close(got_l, ref_l, "q8 full-size lse")

@@ -48,8 +48,7 @@ def _check(w, idx, *, top_k=None, sinks=None, what=""):
     empty = np.isneginf(ref_l)
     assert np.array_equal(np.isneginf(got_l), empty), f"{what}: empty (row, head) pairs differ"
     assert np.all(got_o[empty] == 0.0), f"{what}: empty pairs must give zeros"
-    rms, _ = check_close(got_o[~empty], ref_o[~empty], f"{what} out")
-    assert rms < 5e-3, f"{what}: out relative RMS {rms:.2e}"
+    check_close(got_o[~empty], ref_o[~empty], f"{what} out")
     check_close(got_l[~empty], ref_l[~empty], f"{what} lse")
 
 
@@ -114,15 +113,12 @@ def test_full_in_order_lists_equal_the_dense_path():
     check_close(l_s.cpu().numpy(), l_d.reshape(2, 128).cpu().numpy().astype(np.float64), "sparse vs dense lse")
 
 
-def test_full_size_benched_workload_sampled_rows():
+def test_full_size_benched_workload_all_rows():
     """The benched sparse workload at full size (64 rows, top-k 2048, 128
-    heads), in the launch the benchmark times, checked on sampled rows."""
+    heads), in the launch the benchmark times, every row against the oracle."""
     from paged_mla_decode_03_amd.inputs import named_sparse_workload
     w, lists = named_sparse_workload("sparse_topk_decode", poison=True)
     o, l = _run(w, lists)
-    rows = [0, 17, 40, 63]
-    ref_o, ref_l = reference_sparse_decode(w.q_bits[rows], w.kv_bits, w.kv_dtype, lists[rows], w.bmm1_scale,
-                                           w.bmm2_scale)
-    rms, _ = check_close(o.float().cpu().numpy()[rows], ref_o, "sparse full-size out")
-    assert rms < 5e-3
-    check_close(l.cpu().numpy()[rows], ref_l, "sparse full-size lse")
+    ref_o, ref_l = reference_sparse_decode(w.q_bits, w.kv_bits, w.kv_dtype, lists, w.bmm1_scale, w.bmm2_scale)
+    check_close(o.float().cpu().numpy(), ref_o, "sparse full-size out")
+    check_close(l.cpu().numpy(), ref_l, "sparse full-size lse")
