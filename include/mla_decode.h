@@ -48,7 +48,9 @@ enum {
   MLA_ERR_BAD_SHAPE = 10,        /* batch out of [1, MLA_MAX_BATCH], max_seq_len < 1, num_pages < 1,
                                     total_q * num_heads >= 2^31 - 4 */
   MLA_ERR_HIP = 11,              /* the HIP runtime reported an error at launch */
-  MLA_ERR_NO_DEVICE = 12         /* no usable gfx950 device is current */
+  MLA_ERR_NO_DEVICE = 12,        /* no usable gfx950 device is current */
+  MLA_ERR_SCRATCH_TOO_SMALL = 13 /* mla_decode_paged_noalloc: the launch needs more than
+                                    MLA_NOALLOC_SCRATCH_BYTES of workspace */
 };
 
 enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3FN = 1 };
@@ -249,6 +251,33 @@ size_t mla_decode_paged_ex_workspace_size(const mla_decode_dims_t* dims, int32_t
 
 /* Static, NUL-terminated description of a status code. */
 const char* mla_status_string(int status);
+
+/* Size of the library's own per-device workspace used by mla_decode_paged_noalloc. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mla_decode_paged_noalloc -- mla_decode_paged for callers that cannot
+ * allocate: code under HIP graph capture that may not call hipMalloc, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, meaning,
+ * layouts, kernels and results as mla_decode_paged, minus the workspace: the
+ * call uses instead a workspace the library holds in device memory, a
+ * MLA_NOALLOC_SCRATCH_BYTES array on each device it runs on, kept until the
+ * process ends.  It allocates nothing and frees nothing.
+ *
+ * The first call on a device looks up that device's copy of the array (call
+ * once before capturing a graph).  Every call on one device shares that
+ * device's array: calls that overlap on one device (concurrent streams,
+ * graphs replayed concurrently) race and give undefined results; calls
+ * ordered on one stream are safe.  The array needs no initialisation and
+ * holds nothing between calls.
+ * Returns what mla_decode_paged returns, or MLA_ERR_SCRATCH_TOO_SMALL (nothing
+ * enqueued) when mla_decode_paged_workspace_size() for this shape exceeds
+ * MLA_NOALLOC_SCRATCH_BYTES.
+ */
+int mla_decode_paged_noalloc(const void* q, const void* kv_cache, const int32_t* block_tables,
+                             const int32_t* seq_lens, const int32_t* qo_indptr, int32_t max_seq_len,
+                             int32_t max_q_len, float bmm1_scale, float bmm2_scale, int causal, void* out,
+                             float* lse, const mla_decode_dims_t* dims, void* stream);
 
 /*
  * Test hook, not part of the serving interface: override the persistent grid

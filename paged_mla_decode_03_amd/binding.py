@@ -74,6 +74,9 @@ def load_library():
     lib.mla_decode_paged_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, sz,
                                         ctypes.POINTER(MlaDims), vp, ctypes.POINTER(MlaOptions)]
     lib.mla_decode_paged_ex.restype = ctypes.c_int
+    lib.mla_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, ctypes.c_int, vp, vp,
+                                             ctypes.POINTER(MlaDims), vp]
+    lib.mla_decode_paged_noalloc.restype = ctypes.c_int
     lib.mla_merge_partials.argtypes = [vp, vp, i32, i64, vp, vp, vp]
     lib.mla_merge_partials.restype = ctypes.c_int
     lib.mla_decode_paged_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int]
@@ -133,6 +136,21 @@ def mla_decode_paged(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len
         _ptr(q), _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(qo_indptr), int(max_seq_len),
         int(max_q_len), float(bmm1_scale), float(bmm2_scale), int(bool(causal)), _ptr(out), _ptr(lse),
         _ptr(workspace), int(workspace_bytes), ctypes.byref(dims), stream))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES in include/mla_decode.h
+
+
+def mla_decode_paged_noalloc(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q_len, bmm1_scale,
+                             bmm2_scale, causal, out, lse, dims, stream=None):
+    """Direct call of the no-allocation C entry point (the library's own
+    per-device workspace).  Returns the status."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().mla_decode_paged_noalloc(
+        _ptr(q), _ptr(kv_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(qo_indptr), int(max_seq_len),
+        int(max_q_len), float(bmm1_scale), float(bmm2_scale), int(bool(causal)), _ptr(out), _ptr(lse),
+        ctypes.byref(dims), stream))
 
 
 def mla_decode_paged_ex(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q_len, bmm1_scale,

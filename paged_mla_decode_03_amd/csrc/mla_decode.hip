@@ -1666,6 +1666,31 @@ std::atomic<void*> g_ev_start{nullptr};
 std::atomic<void*> g_ev_decode{nullptr};
 std::atomic<void*> g_ev_stop{nullptr};
 
+// The workspace of mla_decode_paged_noalloc, one copy per device.  Host code
+// never passes the array's name to a kernel: it looks up each device's
+// address once (noalloc_scratch) and passes that.
+__device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[MAX_DEVICES];
+std::mutex g_scratch_mutex;
+
+// Device address of this device's scratch array (looked up on its first use,
+// with the device current), or null on failure.
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return nullptr;
+    p = addr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 int device_grid(int* grid_out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MLA_ERR_NO_DEVICE;
@@ -1767,6 +1792,8 @@ const char* mla_status_string(int status) {
     case MLA_ERR_BAD_SHAPE: return "batch, max_seq_len or num_pages out of range";
     case MLA_ERR_HIP: return "HIP launch error";
     case MLA_ERR_NO_DEVICE: return "no usable HIP device";
+    case MLA_ERR_SCRATCH_TOO_SMALL:
+      return "mla_decode_paged_noalloc: the launch needs more workspace than MLA_NOALLOC_SCRATCH_BYTES";
     default: return "unknown status";
   }
 }
@@ -1896,6 +1923,24 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   if (ev0 != nullptr && ev1 != nullptr) (void)hipEventRecord((hipEvent_t)ev1, s);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
+}
+
+int mla_decode_paged_noalloc(const void* q, const void* kv_cache, const int32_t* block_tables,
+                             const int32_t* seq_lens, const int32_t* qo_indptr, int32_t max_seq_len,
+                             int32_t max_q_len, float bmm1_scale, float bmm2_scale, int causal, void* out,
+                             float* lse, const mla_decode_dims_t* dims, void* stream) {
+  if (dims == nullptr) return MLA_ERR_NULL_POINTER;
+  const int v = validate(dims, max_seq_len, max_q_len, qo_indptr != nullptr);
+  if (v != MLA_OK) return v;
+  int grid = 0;
+  const int gs = device_grid(&grid);
+  if (gs != MLA_OK) return gs;
+  const size_t need = workspace_layout(grid, max_units(dims, max_q_len)).total;
+  if (need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return MLA_ERR_NO_DEVICE;
+  return mla_decode_paged_ex(q, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len, max_q_len, bmm1_scale,
+                             bmm2_scale, causal, out, lse, ws, MLA_NOALLOC_SCRATCH_BYTES, dims, stream, nullptr);
 }
 
 int mla_merge_partials(const void* outs, const float* lses, int32_t num_partials, int64_t items, void* out,

@@ -35,7 +35,7 @@ def test_struct_layout_matches_header():
 
 
 def test_status_strings():
-    for code in range(13):
+    for code in range(14):
         s = binding.mla_status_string(code)
         assert isinstance(s, str) and s
     assert binding.mla_status_string(999) == "unknown status"
