@@ -209,6 +209,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
+// Wait until at most N LDS operations of this wave are outstanding (LDS
+// operations complete in issue order, so the older ones are then done).
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" : : "n"(N) : "memory");
+}
+
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
 
 __device__ __forceinline__ u32x4 lds_read_b128(const uint8_t* smem, uint32_t off) {
@@ -271,15 +279,27 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // mfma_fence() gives the 12 wait states an MFMA result needs before any other
 // instruction reads it.  Back-to-back MFMAs that accumulate into the same
 // registers need none.
+//
+// NOP = false drops the leading s_nop where no operand is written by a VALU
+// instruction (bf16 cache: every A/B operand comes from LDS or was written
+// long before); the emitted assembly is checked for the wait-state rules in
+// the CPU tests.  With an fp8 cache the operands are widened by VALU
+// instructions just before, and the s_nop stays.
+template <bool NOP = true>
 __device__ __forceinline__ void mfma_acc_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+template <bool NOP = true>
 __device__ __forceinline__ void mfma_acc_vgpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+template <bool NOP = true>
 __device__ __forceinline__ f32x16 mfma_first_vgpr(const bf16x8& a, const bf16x8& b) {
   f32x16 d;
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  if constexpr (NOP) asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
 __device__ __forceinline__ void mfma_fence(f32x16& v) { asm volatile("s_nop 7\n\ts_nop 3" : "+v"(v)); }
@@ -863,7 +883,8 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   };
   // QK^T of the tile in buf.  fill(k) runs right after MFMA k: independent VALU
   // work (the previous tile's softmax) that the wave issues while the matrix
-  // core is busy; the scheduling barrier keeps each piece in its slot.
+  // core is busy; the scheduling barrier keeps each piece in its slot.  pre()
+  // runs once the first A fragments are requested, before the first MFMA.
   // fp8 query: A fragment of 64-dim step kk (0..7 latent, 8 RoPE) is 32 bytes
   // of the lane's row, chunks 4kk + 2h and 4kk + 2h + 1 (RoPE: 2h, 2h + 1), the
   // same bytes the lane's query fragment holds, so the MFMA pairs them
@@ -883,7 +904,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     const u32x4 y = lds_read_b128(smem, o1);
     return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
   };
-  auto qk = [&](uint32_t buf_in, auto&& fill) -> f32x16 {
+  auto qk = [&](uint32_t buf_in, auto&& fill, auto&& pre) -> f32x16 {
     const uint32_t buf = opaque(buf_in);
     f32x16 s;
     if constexpr (Q8) {
@@ -893,6 +914,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       i32x8 araw8[GA8];
 #pragma unroll
       for (int k = 0; k < GA8; ++k) araw8[k] = load_a8(buf, k);
+      pre();
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         const i32x8 cur = araw8[k % GA8];
@@ -915,12 +937,13 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       u32x4 araw[GA];
 #pragma unroll
       for (int k = 0; k < GA; ++k) araw[k] = load_a(buf, k);
+      pre();
 #pragma unroll
       for (int k = 0; k < QK_STEPS; ++k) {
         const u32x4 cur = araw[k % GA];
         if (k + GA < QK_STEPS) araw[k % GA] = load_a(buf, k + GA);
-        if (k == 0) s = mfma_first_vgpr(to_bf16(cur), qf[k]);
-        else mfma_acc_vgpr(s, to_bf16(cur), qf[k]);
+        if (k == 0) s = mfma_first_vgpr<FP8>(to_bf16(cur), qf[k]);
+        else mfma_acc_vgpr<FP8>(s, to_bf16(cur), qf[k]);
         fill(k);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -930,6 +953,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   };
   static_assert(!Q8 || FP8, "an fp8 query needs the fp8 cache");
   auto no_fill = [](int) {};
+  auto no_pre = [] {};
 
   // Tile t has landed once at most the DMA ops of the n tiles issued after it
   // remain; a partial tile among them makes the count unknown, so drain.
@@ -1028,7 +1052,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   wait_lgkm0();
   block_barrier();  // tile t0 is in LDS
   f32x16 s_next{};
-  if (ACTIVE) s_next = qk(buf_of(t0), no_fill);
+  if (ACTIVE) s_next = qk(buf_of(t0), no_fill, no_pre);
   const TileLoad no_load{nullptr, 0u, 0u};
   for (int t = t0; t < t1; ++t) {
     const f32x16 s = s_next;
@@ -1050,35 +1074,41 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
       // Tile t+3 goes to the buffer of tile t-1.  Even waves issue their share
       // now, odd waves at the P exchange below: two bursts of loads queue in the
       // CU's address unit instead of one burst from all four waves.
-      if constexpr (PS == 0) {
-        // sparse: every wave now, its share of tile t+3 then the entries of t+5
-        if (t + 3 < t1) {
-          issue_sparse_share<FP8>(p, smem, buf_of(t + 3), t + 3);
-          issue_sparse_index(p, smem, b, t + 5, t + 5 < t1);
-        }
-      } else {
-        if (t + 3 < t1) {
-          tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
-          if ((w & 1) == 0 || !ACTIVE) {
-            issue_tile_share<FP8>(tl);
-            tl = no_load;
+      // (active waves run this once the first A fragments of QK^T(t+1) are on
+      // their way, so the tile preparation and the DMA issue overlap their
+      // latency)
+      auto load_ahead = [&] {
+        if constexpr (PS == 0) {
+          // sparse: every wave now, its share of tile t+3 then the entries of t+5
+          if (t + 3 < t1) {
+            issue_sparse_share<FP8>(p, smem, buf_of(t + 3), t + 3);
+            issue_sparse_index(p, smem, b, t + 5, t + 5 < t1);
+          }
+        } else {
+          if (t + 3 < t1) {
+            tl = prepare_tile<FP8, PS>(p, smem, buf_of(t + 3), b, L, t + 3, pw);
+            if ((w & 1) == 0 || !ACTIVE) {
+              issue_tile_share<FP8>(tl);
+              tl = no_load;
+            }
           }
         }
-      }
+      };
+      if (!ACTIVE) load_ahead();
       if (ACTIVE) {
         if (fast && (!FP8 || Q8)) {
           const float nm = -st.m_ref;
-          s_next = qk(buf_of(t + 1), [&](int k) { fast_piece(s, nm, k); });
+          s_next = qk(buf_of(t + 1), [&](int k) { fast_piece(s, nm, k); }, load_ahead);
         } else if (fast) {
           // fp8: the A operands' widening already fills the VALU slots between
           // the MFMAs, so the softmax goes first
           const float nm = -st.m_ref;
 #pragma unroll
           for (int k = 0; k < QK_STEPS; ++k) fast_piece(s, nm, k);
-          s_next = qk(buf_of(t + 1), no_fill);
+          s_next = qk(buf_of(t + 1), no_fill, load_ahead);
         } else {
           masked_softmax(s, t, live);
-          s_next = qk(buf_of(t + 1), no_fill);
+          s_next = qk(buf_of(t + 1), no_fill, load_ahead);
         }
       }
     } else if (ACTIVE) {
@@ -1097,17 +1127,21 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     }
     // ---------------- P exchange: the partner wave (w ^ 1) owns the other 32
     // pairs of this 64-pair group; each wave posts its P and reads the
-    // partner's.  The first V^T fragments are read across the barrier.
+    // partner's.  The P write goes first and the barrier waits for it alone:
+    // the first V^T fragments, read after it, stay in flight across the
+    // barrier (their latency overlaps the barrier and the odd waves' DMA).
     const uint32_t buf = opaque(buf_of(t));
     constexpr int GV = 4;  // V^T fragments read this many steps ahead
+    constexpr int V_READS = GV * (FP8 ? 1 : 2);  // LDS reads of those fragments
+    *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own) = pc0;
+    *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own + 1024) =
+        pc1;
+    asm volatile("" ::: "memory");  // the P write stays ahead of the V^T reads
     u32x4 vraw[GV];
 #pragma unroll
     for (int i = 0; i < GV; ++i) vraw[i] = load_v(buf, i);
     issue_tile_share<FP8>(tl);
-    *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own) = pc0;
-    *(__attribute__((address_space(3))) bf16x8*)((__attribute__((address_space(3))) uint8_t*)smem + ps_own + 1024) =
-        pc1;
-    wait_lgkm0();
+    wait_lgkm<V_READS>();  // the two P writes have landed
     block_barrier();  // P of tile t posted
     const bf16x8 pp0 = *(const __attribute__((address_space(3))) bf16x8*)(
         (const __attribute__((address_space(3))) uint8_t*)smem + ps_other);
@@ -1119,13 +1153,13 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     // the partner's P is still on its way.
 #pragma unroll
     for (int step = 0; step < GV; ++step)
-      mfma_acc_agpr(st.acc[2 * (step & 7)], to_bf16(vraw[step]), pc0);
+      mfma_acc_agpr<FP8>(st.acc[2 * (step & 7)], to_bf16(vraw[step]), pc0);
 #pragma unroll
     for (int step = 0; step < PV_BLOCKS; ++step) {
       const int d = step & 7;
       const bf16x8 v = to_bf16(vraw[step % GV]);
-      if (step >= GV) mfma_acc_agpr(st.acc[2 * d], v, (step >> 3) ? pc1 : pc0);
-      mfma_acc_agpr(st.acc[2 * d + 1], v, (step >> 3) ? pp1 : pp0);
+      if (step >= GV) mfma_acc_agpr<FP8>(st.acc[2 * d], v, (step >> 3) ? pc1 : pc0);
+      mfma_acc_agpr<FP8>(st.acc[2 * d + 1], v, (step >> 3) ? pp1 : pp0);
       if (step + GV < PV_BLOCKS) vraw[step % GV] = load_v(buf, step + GV);
     }
     // results land before anything but the next tile's MFMAs can touch them
