@@ -11,10 +11,11 @@ headline, uniform spec 1+3 causal, ragged packed causal, long-context fp8 KV)
 is timed in turn, each with its own warmup and timed steps, the headline
 last; the one JSON line carries the headline's figures and, under "configs",
 each workload's.  Per workload: KV-tokens/s, TFLOP/s and algorithmic GB/s
-over the timed steps, and the roofline fraction of the launch (algorithmic
-bytes or flops over the mean device time from the first kernel's start to the
-last kernel's end, HIP events on the launch stream), plus the decode kernel's
-own fraction.  The float64 CPU oracle is timed on a bounded sample of the
+over the timed steps, and the roofline fraction of a step (algorithmic bytes
+or flops over the device time per step of the timed region, from two HIP
+events on the launch stream around it: every kernel of a launch and the gaps
+between launches count), plus the decode kernel's own fraction from a
+separate pass with events inside each launch.  The float64 CPU oracle is timed on a bounded sample of the
 headline workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
@@ -116,33 +117,43 @@ def profiled_traffic(workload):
 
 
 def time_steps(step, steps, warmup):
-    """Run warmup untimed steps, then time exactly `steps` steps (bracketed by
-    device synchronisation), the library recording HIP events on the launch
-    stream before its first kernel, after the decode kernel and after its
-    last kernel.  Returns (ms per step, mean launch ms, mean decode-kernel ms)."""
+    """Run warmup untimed steps, then time exactly `steps` steps, bracketed by
+    device synchronisation and by two HIP events on the launch stream (torch's
+    current stream, which the steps launch on), with nothing else inside the
+    region.  A second pass of as many steps, outside the timed region, has the
+    library record events inside every launch, before the decode kernel and
+    right after it: those records add a few microseconds to a step, so they
+    stay out of the timed one.  Returns (wall ms per step, device ms per step
+    over the timed region, mean decode-kernel ms)."""
     import numpy as np
     import torch
     from paged_mla_decode_03_amd import binding
     log(f"[bench] warmup {warmup}")
     for _ in range(warmup):
         step()
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
+    log(f"[bench] timing {steps} steps")
+    t0 = time.perf_counter()
+    region[0].record()
+    for _ in range(steps):
+        step()
+    region[1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    device_ms = region[0].elapsed_time(region[1]) / steps
     ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     for trio in ev:
         for e in trio:
             e.record()
     torch.cuda.synchronize()
-    log(f"[bench] timing {steps} steps")
-    t0 = time.perf_counter()
     for i in range(steps):
         binding.set_kernel_events(ev[i][0], ev[i][2], ev[i][1])
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     binding.set_kernel_events(None, None)
-    launch = float(np.mean([a.elapsed_time(c) for a, b, c in ev]))
     decode = float(np.mean([a.elapsed_time(b) for a, b, c in ev]))
-    return (t1 - t0) * 1e3 / steps, launch, decode
+    return (t1 - t0) * 1e3 / steps, device_ms, decode
 
 
 def roofline(counts, kern_ms, name, q8=False):
@@ -190,8 +201,8 @@ def sparse_cpu_baseline(w, lists, budget_s=10.0):
                       f"in {dt:.1f} s, float64 NumPy"}
 
 
-def _result(name, counts, ms_step, launch_ms, decode_ms, steps, warmup, dtype, data, config, q8=False):
-    roof = roofline(counts, launch_ms, name, q8=q8)
+def _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup, dtype, data, config, q8=False):
+    roof = roofline(counts, device_ms, name, q8=q8)
     dec = roofline(counts, decode_ms, name, q8=q8)
     return {
         "metric": METRIC,
@@ -209,7 +220,7 @@ def _result(name, counts, ms_step, launch_ms, decode_ms, steps, warmup, dtype, d
         "config": config,
         "tflops": counts["flops"] / (ms_step * 1e-3) / 1e12,
         "gbps": counts["bytes"] / (ms_step * 1e-3) / 1e9,
-        "launch_ms": launch_ms,
+        "device_ms_per_step": device_ms,
         "decode_kernel_ms": decode_ms,
         "decode_kernel_frac": dec["frac"],
         "kernel_source_sha256": kernel_source_sha256(),
@@ -263,13 +274,13 @@ def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
-    ms_step, launch_ms, decode_ms = time_steps(step, steps, warmup)
+    ms_step, device_ms, decode_ms = time_steps(step, steps, warmup)
     config = {"workload": name, "rows": w.total_q, "heads": w.num_heads, "top_k": K,
               "seq_lens": list(spec["seq_len_range"]), "page_size": w.page_size, "kv_dtype": w.kv_dtype,
               "lse": w.want_lse, "kv_tokens": counts["kv_tokens"]}
     data = (f"synthetic (seeded N(0,1) q/kv, shuffled pages, seeded top-k selections of each request; "
             f"{max(1, rotate)} cache copies rotated across steps)")
-    res = _result(name, counts, ms_step, launch_ms, decode_ms, steps, warmup,
+    res = _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup,
                   "bf16" if w.kv_dtype == "bf16" else "fp8 e4m3 KV widened exactly to bf16, bf16 MFMA",
                   data, config)
     if want_cpu:
@@ -326,7 +337,7 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
-    ms_step, launch_ms, decode_ms = time_steps(step, steps, warmup)
+    ms_step, device_ms, decode_ms = time_steps(step, steps, warmup)
     spec = WORKLOADS[base]
     config = {"workload": name, "batch": B, "heads": H, **({"q_dtype": "fp8_e4m3fn"} if q8 else {}),
               "q_len": spec.get("q_len") if "q_len_range" not in spec else list(spec["q_len_range"]),
@@ -336,7 +347,7 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
               "kv_tokens": counts["kv_tokens"]}
     data = (f"synthetic (seeded N(0,1) q/kv, shuffled pages; {max(1, rotate)} cache copies rotated across steps)"
             + ("; query rounded to fp8 E4M3FN, q_scale 1" if q8 else ""))
-    res = _result(name, counts, ms_step, launch_ms, decode_ms, steps, warmup, _dtype_label(w.kv_dtype, q8), data,
+    res = _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup, _dtype_label(w.kv_dtype, q8), data,
                   config, q8=q8)
     if want_cpu:
         log("[bench] cpu baseline (oracle)")
@@ -346,7 +357,7 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
 
 def _summary(r):
     """The per-workload figures carried under "configs" of the JSON line."""
-    keep = ("value", "unit", "ms_per_step", "launch_ms", "decode_kernel_ms", "decode_kernel_frac", "tflops", "gbps",
+    keep = ("value", "unit", "ms_per_step", "device_ms_per_step", "decode_kernel_ms", "decode_kernel_frac", "tflops", "gbps",
             "dtype", "roofline")
     d = {k: r[k] for k in keep}
     d["kv_tokens"] = r["config"]["kv_tokens"]
