@@ -1175,8 +1175,12 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
 template <bool FP8, int PS, int QM>
 __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, int b, int pb, int L, int t0, int t1,
                                                 int slot, float& m_seed) {
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
+  // (an opaque thread id: lane-derived values are recomputed for every
+  // segment instead of being held, or spilled, across the whole kernel)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
   const int h = lane >> 5;
   const int col = lane & 31;
   int r0;
