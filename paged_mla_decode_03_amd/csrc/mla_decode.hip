@@ -266,6 +266,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// Two floats -> two bf16 (round to nearest even) in one dword, a in the low
+// half: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // ---------------------------------------------------------------- matrix-core ops
 //
 // The MFMAs are issued through inline asm so that the register class of each
@@ -1348,9 +1354,8 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   // relative to m_ref; the merge kernel divides by the summed denominator).
   // It is staged in LDS (the tile buffers are all consumed) as the unit's
   // [128 pairs][512 dims] block, 16-byte chunk c of row r at chunk c ^ (r & 15),
-  // so that each wave then stores whole 1 KB rows.  The accumulators go out one
-  // 32-dim block at a time: the empty asm keeps each block in AGPRs until its
-  // turn, so only 16 of them are copied to VGPRs at once.
+  // so that each wave then stores whole 1 KB rows.  Each accumulator is read
+  // out of its AGPR once and pairs of values go to bf16 in one conversion.
   const float lsum = sum_halves(st.lsum);
   if (active) {
     const int dh = w & 1;
@@ -1361,7 +1366,6 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
       const uint32_t rowb = (uint32_t)r * (D_V * 2) + 8 * h;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        asm volatile("" : "+a"(st.acc[2 * d + j]));
         const f32x16 v = st.acc[2 * d + j];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -1369,11 +1373,7 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
           const int chunk = 32 * dh + 4 * d + q4;
           u32x2 packed;
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const __bf16 lo = (__bf16)v[4 * q4 + 2 * e];
-            const __bf16 hi = (__bf16)v[4 * q4 + 2 * e + 1];
-            packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          }
+          for (int e = 0; e < 2; ++e) packed[e] = pack_bf16x2(v[4 * q4 + 2 * e], v[4 * q4 + 2 * e + 1]);
           *(__attribute__((address_space(3))) u32x2*)((__attribute__((address_space(3))) uint8_t*)smem + rowb +
                                                      16 * (chunk ^ (r & 15))) = packed;
         }
@@ -1624,11 +1624,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const float inv = empty ? 0.f : ((p.bmm2_dev != nullptr) ? *p.bmm2_dev : p.bmm2) / den;
   u32x4 packed;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 lo = (__bf16)(acc[2 * e] * inv);
-    const __bf16 hi = (__bf16)(acc[2 * e + 1] * inv);
-    packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
+  for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
   *(u32x4*)(p.out + (size_t)item * D_V + 8 * lane) = packed;
   if (p.lse != nullptr && lane == 0) p.lse[item] = empty ? -INFINITY : (M + __log2f(den)) * LN2;
 }
@@ -1675,11 +1671,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_partials_kernel(const
   const float inv = empty ? 0.f : 1.f / den;
   u32x4 packed;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 lo = (__bf16)(acc[2 * e] * inv);
-    const __bf16 hi = (__bf16)(acc[2 * e + 1] * inv);
-    packed[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
+  for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
   *(u32x4*)(out + item * D_V + 8 * lane) = packed;
   if (lse != nullptr && lane == 0) lse[item] = empty ? -INFINITY : M + __logf(den);
 }
