@@ -249,6 +249,49 @@ size_t mla_decode_paged_workspace_size(const mla_decode_dims_t* dims, int32_t ma
 size_t mla_decode_paged_ex_workspace_size(const mla_decode_dims_t* dims, int32_t max_seq_len, int32_t max_q_len,
                                           int want_lse, const mla_decode_options_t* opts);
 
+/*
+ * Bits of the word mla_decode_check_contract writes; 0 means the checked part
+ * of the contract holds.
+ */
+#define MLA_CONTRACT_SEQ_LEN (1u << 0)  /* some seq_lens[b] < 1 or > max_seq_len */
+#define MLA_CONTRACT_QO_START (1u << 1) /* qo_indptr[0] != 0 */
+#define MLA_CONTRACT_QO_ORDER (1u << 2) /* some qo_indptr[b + 1] <= qo_indptr[b] */
+#define MLA_CONTRACT_QO_END (1u << 3)   /* qo_indptr[B] != total_q */
+#define MLA_CONTRACT_Q_LEN (1u << 4)    /* some request has more than max_q_len query rows */
+#define MLA_CONTRACT_CAUSAL (1u << 5)   /* causal, and some request has more query rows than seq_lens[b] */
+#define MLA_CONTRACT_PAGE_ID (1u << 6)  /* a block-table entry a launch would read is < 0 or >= num_pages */
+
+/*
+ * mla_decode_check_contract -- a test and debugging aid, not part of the
+ * decode path: checks on the device the part of a launch's contract that
+ * lives in device memory (FlashInfer docs,
+ * "prims_ts_batch_decode_with_kv_cache_mla", contract paragraph: positive
+ * lengths no larger than the static bound, query offsets that start at 0,
+ * increase strictly and end at total_q with steps no larger than max_q_len,
+ * causal requests with no more query rows than cached rows, page ids inside
+ * the cache).  mla_decode_paged never checks these; a violation there gives
+ * undefined results.
+ *
+ * Arguments are those of mla_decode_paged with the same meaning (dims: batch,
+ * q_len_fixed, total_q, page_size, num_pages and block_table_stride are used).
+ * Reads seq_lens[0 .. B), qo_indptr[0 .. B] (if not NULL) and, of row b of
+ * block_tables, entries 0 .. min(ceil(seq_lens[b] / page_size),
+ * block_table_stride) - 1 only (the entries a launch reads).  Writes
+ * result[0] = the OR of the MLA_CONTRACT_* bits violated and result[1] = 1 +
+ * the lowest request index with a violation (0 if none); result is device
+ * memory, 4-byte aligned, owned by the caller.  In the sequence-sharded mode
+ * of mla_decode_paged_ex a local length of 0 is allowed but reads here as
+ * MLA_CONTRACT_SEQ_LEN.  One workgroup, asynchronous on `stream`, allocates
+ * nothing.  Returns MLA_OK, MLA_ERR_NULL_POINTER, MLA_ERR_MISALIGNED,
+ * MLA_ERR_BAD_SHAPE (batch out of [1, MLA_MAX_BATCH], num_pages < 1,
+ * block_table_stride < 1 or max_seq_len < 1), MLA_ERR_BAD_PAGE_SIZE,
+ * MLA_ERR_BAD_Q_LEN (max_q_len < 1, total_q < 1, or a fixed launch with
+ * q_len_fixed < 1) or MLA_ERR_HIP.
+ */
+int mla_decode_check_contract(const int32_t* block_tables, const int32_t* seq_lens, const int32_t* qo_indptr,
+                              int32_t max_seq_len, int32_t max_q_len, int causal, const mla_decode_dims_t* dims,
+                              uint32_t* result, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* mla_status_string(int status);
 

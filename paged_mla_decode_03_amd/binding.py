@@ -79,6 +79,8 @@ def load_library():
     lib.mla_decode_paged_noalloc.restype = ctypes.c_int
     lib.mla_merge_partials.argtypes = [vp, vp, i32, i64, vp, vp, vp]
     lib.mla_merge_partials.restype = ctypes.c_int
+    lib.mla_decode_check_contract.argtypes = [vp, vp, vp, i32, i32, ctypes.c_int, ctypes.POINTER(MlaDims), vp, vp]
+    lib.mla_decode_check_contract.restype = ctypes.c_int
     lib.mla_decode_paged_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int]
     lib.mla_decode_paged_workspace_size.restype = sz
     lib.mla_decode_paged_ex_workspace_size.argtypes = [ctypes.POINTER(MlaDims), i32, i32, ctypes.c_int,
@@ -442,3 +444,39 @@ def merge_partials(outs, lses, out=None, lse=None):
     if rc != MLA_OK:
         raise RuntimeError(f"mla_merge_partials failed: {mla_status_string(rc)} (status {rc})")
     return out, lse
+
+
+# Bits of mla_decode_check_contract's result word (MLA_CONTRACT_* in include/mla_decode.h).
+CONTRACT_BITS = {
+    "seq_len": 1 << 0,
+    "qo_start": 1 << 1,
+    "qo_order": 1 << 2,
+    "qo_end": 1 << 3,
+    "q_len": 1 << 4,
+    "causal": 1 << 5,
+    "page_id": 1 << 6,
+}
+
+
+def check_contract(query, kv_cache, block_tables, seq_lens, max_seq_len, *, qo_indptr=None, max_seq_len_q=None,
+                   causal=False):
+    """Test and debugging aid: run the library's device-side check of the
+    launch contract held in device memory (lengths, query offsets, causal
+    lengths, page ids) for the arguments decode() would get, and return
+    (set of violated rule names, lowest offending request or None).  Waits for
+    the check to finish; it is not part of the decode path."""
+    dims, max_q, _, _ = dims_for(query, kv_cache, block_tables, seq_lens, qo_indptr, max_seq_len_q)
+    dev = seq_lens.device
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens), ("qo_indptr", qo_indptr)):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.device != dev):
+            raise TypeError(f"{name} must be a contiguous int32 tensor on {dev}")
+    result = torch.zeros(2, dtype=torch.int32, device=dev)
+    rc = load_library().mla_decode_check_contract(block_tables.data_ptr(), seq_lens.data_ptr(),
+                                                  None if qo_indptr is None else qo_indptr.data_ptr(),
+                                                  int(max_seq_len), int(max_q), int(bool(causal)), ctypes.byref(dims),
+                                                  result.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+    if rc != MLA_OK:
+        raise RuntimeError(f"mla_decode_check_contract failed: {mla_status_string(rc)} (status {rc})")
+    bits, first = (int(v) & 0xFFFFFFFF for v in result.cpu().tolist())
+    return {n for n, m in CONTRACT_BITS.items() if bits & m}, (first - 1 if first else None)
+

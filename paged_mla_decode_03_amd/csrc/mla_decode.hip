@@ -1676,6 +1676,77 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_partials_kernel(const
   if (lse != nullptr && lane == 0) lse[item] = empty ? -INFINITY : M + __logf(den);
 }
 
+// Contract check (FlashInfer docs, "prims_ts_batch_decode_with_kv_cache_mla",
+// contract paragraph: the part of a launch's contract held in device memory).
+// One workgroup: every thread takes requests b = tid, tid + 1024, ... for the
+// length and offset rules, then the block-table entries a launch would read
+// (0 .. ceil(L_b / page_size) - 1, at most the row's width), 1024 at a time.
+// Violation bits and the lowest offending request meet in LDS; thread 0
+// writes result[0] = bits, result[1] = that request + 1 (0: none).
+struct ContractArgs {
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qo_indptr;
+  uint32_t* result;
+  int64_t num_pages;
+  int32_t batch, bt_stride, page_size, max_seq_len, max_q_len, q_len_fixed, total_q, causal;
+};
+
+constexpr int CHECK_THREADS = 1024;
+
+__global__ __launch_bounds__(CHECK_THREADS) void mla_check_contract_kernel(ContractArgs c) {
+  __shared__ uint32_t s_bits;
+  __shared__ int s_first;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_bits = 0;
+    s_first = c.batch;
+  }
+  __syncthreads();
+  uint32_t bits = 0;
+  int first = c.batch;
+  for (int b = tid; b < c.batch; b += CHECK_THREADS) {
+    uint32_t v = 0;
+    const int L = c.seq_lens[b];
+    if (L < 1 || L > c.max_seq_len) v |= MLA_CONTRACT_SEQ_LEN;
+    int qb = c.q_len_fixed;
+    if (c.qo_indptr != nullptr) {
+      const int a = c.qo_indptr[b], e = c.qo_indptr[b + 1];
+      if (b == 0 && a != 0) v |= MLA_CONTRACT_QO_START;
+      if (e <= a) v |= MLA_CONTRACT_QO_ORDER;
+      if (b == c.batch - 1 && e != c.total_q) v |= MLA_CONTRACT_QO_END;
+      qb = e - a;
+    }
+    if (qb > c.max_q_len) v |= MLA_CONTRACT_Q_LEN;
+    if (c.causal && qb > L) v |= MLA_CONTRACT_CAUSAL;
+    if (v != 0) {
+      bits |= v;
+      first = min(first, b);
+    }
+  }
+  for (int b = 0; b < c.batch; ++b) {
+    const int64_t L = max(c.seq_lens[b], 0);
+    const int np = (int)min((L + c.page_size - 1) / c.page_size, (int64_t)c.bt_stride);
+    const int32_t* row = c.block_tables + (size_t)b * c.bt_stride;
+    for (int j = tid; j < np; j += CHECK_THREADS) {
+      const int32_t id = row[j];
+      if (id < 0 || (int64_t)id >= c.num_pages) {
+        bits |= MLA_CONTRACT_PAGE_ID;
+        first = min(first, b);
+      }
+    }
+  }
+  if (bits != 0) {
+    atomicOr(&s_bits, bits);
+    atomicMin(&s_first, first);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    c.result[0] = s_bits;
+    c.result[1] = s_first < c.batch ? (uint32_t)s_first + 1u : 0u;
+  }
+}
+
 // Conversion check: the exact fp8 -> bf16 widening the decode kernel uses, on
 // n groups of 8 codes (test hook).
 __global__ void fp8_to_bf16_kernel(const u32x2* in, bf16x8* out, int64_t n) {
@@ -1982,6 +2053,35 @@ int mla_merge_partials(const void* outs, const float* lses, int32_t num_partials
   if (blocks > 0x7fffffff) return MLA_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(mla_merge_partials_kernel, dim3((unsigned)blocks), dim3(MERGE_THREADS), 0, (hipStream_t)stream,
                      (const uint16_t*)outs, lses, (int)num_partials, items, (uint16_t*)out, lse);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_decode_check_contract(const int32_t* block_tables, const int32_t* seq_lens, const int32_t* qo_indptr,
+                              int32_t max_seq_len, int32_t max_q_len, int causal, const mla_decode_dims_t* dims,
+                              uint32_t* result, void* stream) {
+  if (!block_tables || !seq_lens || !dims || !result) return MLA_ERR_NULL_POINTER;
+  if ((uintptr_t)result & 3) return MLA_ERR_MISALIGNED;
+  if (dims->batch < 1 || dims->batch > MLA_MAX_BATCH || dims->num_pages < 1 || dims->block_table_stride < 1 ||
+      max_seq_len < 1)
+    return MLA_ERR_BAD_SHAPE;
+  if (dims->page_size != 16 && dims->page_size != 32 && dims->page_size != 64) return MLA_ERR_BAD_PAGE_SIZE;
+  if (max_q_len < 1 || dims->total_q < 1 || (qo_indptr == nullptr && dims->q_len_fixed < 1)) return MLA_ERR_BAD_Q_LEN;
+  ContractArgs c;
+  c.block_tables = block_tables;
+  c.seq_lens = seq_lens;
+  c.qo_indptr = qo_indptr;
+  c.result = result;
+  c.num_pages = dims->num_pages;
+  c.batch = dims->batch;
+  c.bt_stride = dims->block_table_stride;
+  c.page_size = dims->page_size;
+  c.max_seq_len = max_seq_len;
+  c.max_q_len = max_q_len;
+  c.q_len_fixed = dims->q_len_fixed;
+  c.total_q = dims->total_q;
+  c.causal = causal != 0;
+  hipLaunchKernelGGL(mla_check_contract_kernel, dim3(1), dim3(CHECK_THREADS), 0, (hipStream_t)stream, c);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }

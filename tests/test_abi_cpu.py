@@ -165,3 +165,29 @@ def test_fp8_query_option_rejects_bad_combinations():
     assert ex(_dims(kv_dtype=1), q8) == NO_DEVICE           # fp8 query and fp8 cache: accepted
     sq8 = binding.MlaOptions(None, None, None, None, 1, 0, 4, 1)
     assert ex(_dims(kv_dtype=1), sq8) == BAD_SHAPE          # not in the sparse layout
+
+
+def test_contract_check_rejects_bad_arguments():
+    """mla_decode_check_contract: every host-side rejection comes before any
+    device call."""
+    lib = binding.load_library()
+
+    def chk(bt=FAKE, sl=FAKE, qo=None, max_seq_len=128, max_q_len=1, dims=None, result=FAKE):
+        d = dims if dims is not None else _dims()
+        return lib.mla_decode_check_contract(bt, sl, qo, max_seq_len, max_q_len, 1, ctypes.byref(d), result, None)
+
+    NULL, SHAPE, PAGE, QLEN, MIS = 1, 10, 3, 8, 6
+    assert chk(bt=None) == NULL
+    assert chk(sl=None) == NULL
+    assert chk(result=None) == NULL
+    assert lib.mla_decode_check_contract(FAKE, FAKE, None, 128, 1, 1, None, FAKE, None) == NULL
+    assert chk(result=FAKE + 2) == MIS
+    assert chk(dims=_dims(batch=0)) == SHAPE
+    assert chk(dims=_dims(batch=1025)) == SHAPE
+    assert chk(dims=_dims(num_pages=0)) == SHAPE
+    assert chk(dims=_dims(block_table_stride=0)) == SHAPE
+    assert chk(max_seq_len=0) == SHAPE
+    assert chk(dims=_dims(page_size=48)) == PAGE
+    assert chk(max_q_len=0) == QLEN
+    assert chk(dims=_dims(total_q=0)) == QLEN
+    assert chk(dims=_dims(q_len_fixed=0)) == QLEN
