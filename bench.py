@@ -358,8 +358,8 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
 
 def _summary(r):
     """The per-workload figures carried under "configs" of the JSON line."""
-    keep = ("value", "unit", "ms_per_step", "device_ms_per_step", "decode_kernel_ms", "decode_kernel_frac", "tflops", "gbps",
-            "dtype", "roofline")
+    keep = ("value", "unit", "ms_per_step", "device_ms_per_step", "decode_kernel_ms", "decode_kernel_frac", "tflops",
+            "gbps", "dtype", "roofline")
     d = {k: r[k] for k in keep}
     d["kv_tokens"] = r["config"]["kv_tokens"]
     return d
