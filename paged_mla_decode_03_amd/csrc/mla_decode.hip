@@ -794,10 +794,16 @@ struct SegState {
 // 1 = fp8 query codes on the fp8 MFMA; 2 = bf16 query split into two fp8 terms
 // (q 2^e = q_hi + q_lo) on the fp8 MFMA, for an fp8 cache.  c is the logit
 // scale in log2 units of the lane's scores (mode 2: divided by 2^e).
-template <bool FP8, int PS, bool ACTIVE, int QM, typename QF>
+// OWN / PARTNER: some pair of this wave's / the partner's 32 QK^T pairs
+// exists.  In an active group the even wave's pairs always do; when the odd
+// wave's do not (a unit of at most 32, or 65 to 96, pairs), the odd wave skips
+// its QK^T and softmax and both waves skip the P.V MFMAs of those pairs, whose
+// results would be discarded.
+template <bool FP8, int PS, bool ACTIVE, int QM, bool OWN, bool PARTNER, typename QF>
 __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int b, int L, int t0, int t1,
                                              const QF& qf, float c, int n_vis, int min_vis,
                                              SegState& st, PageWin& pw) {
+  static_assert(!ACTIVE || OWN || PARTNER, "an active group has live pairs");
   constexpr bool Q8 = QM != 0;
   constexpr int LOADS = tile_loads<FP8>();
   const int lane = threadIdx.x & 63;
@@ -1058,7 +1064,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
   wait_lgkm0();
   block_barrier();  // tile t0 is in LDS
   f32x16 s_next{};
-  if (ACTIVE) s_next = qk(buf_of(t0), no_fill, no_pre);
+  if (ACTIVE && OWN) s_next = qk(buf_of(t0), no_fill, no_pre);
   const TileLoad no_load{nullptr, 0u, 0u};
   for (int t = t0; t < t1; ++t) {
     const f32x16 s = s_next;
@@ -1100,8 +1106,8 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
           }
         }
       };
-      if (!ACTIVE) load_ahead();
-      if (ACTIVE) {
+      if (!ACTIVE || !OWN) load_ahead();
+      if (ACTIVE && OWN) {
         if (fast && (!FP8 || Q8)) {
           const float nm = -st.m_ref;
           s_next = qk(buf_of(t + 1), [&](int k) { fast_piece(s, nm, k); }, load_ahead);
@@ -1117,7 +1123,7 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
           s_next = qk(buf_of(t + 1), no_fill, load_ahead);
         }
       }
-    } else if (ACTIVE) {
+    } else if (ACTIVE && OWN) {
       if (fast) {
         const float nm = -st.m_ref;
 #pragma unroll
@@ -1156,16 +1162,20 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     // ---------------- O^T (this wave's 256 dims) += V^T . P^T for the wave's own
     // 32 pairs (acc[2d]) and the partner's (acc[2d + 1]): each V^T fragment
     // feeds two MFMAs.  The own-P MFMAs of the first GV steps go first, while
-    // the partner's P is still on its way.
+    // the partner's P is still on its way.  A half with no live pair is skipped.
+    if constexpr (OWN) {
 #pragma unroll
-    for (int step = 0; step < GV; ++step)
-      mfma_acc_agpr<FP8>(st.acc[2 * (step & 7)], to_bf16(vraw[step]), pc0);
+      for (int step = 0; step < GV; ++step)
+        mfma_acc_agpr<FP8>(st.acc[2 * (step & 7)], to_bf16(vraw[step]), pc0);
+    }
 #pragma unroll
     for (int step = 0; step < PV_BLOCKS; ++step) {
       const int d = step & 7;
       const bf16x8 v = to_bf16(vraw[step % GV]);
-      if (step >= GV) mfma_acc_agpr<FP8>(st.acc[2 * d], v, (step >> 3) ? pc1 : pc0);
-      mfma_acc_agpr<FP8>(st.acc[2 * d + 1], v, (step >> 3) ? pp1 : pp0);
+      if constexpr (OWN) {
+        if (step >= GV) mfma_acc_agpr<FP8>(st.acc[2 * d], v, (step >> 3) ? pc1 : pc0);
+      }
+      if constexpr (PARTNER) mfma_acc_agpr<FP8>(st.acc[2 * d + 1], v, (step >> 3) ? pp1 : pp0);
       if (step + GV < PV_BLOCKS) vraw[step % GV] = load_v(buf, step + GV);
     }
     // results land before anything but the next tile's MFMAs can touch them
@@ -1330,8 +1340,15 @@ __device__ __forceinline__ bool process_segment(const Params& p, uint8_t* smem, 
   st.s_max = -INFINITY;
   st.lsum = 0.f;
   st.ref_ready = __builtin_amdgcn_ballot_w64(m_seed == -INFINITY) == 0;
-  if (active) segment_loop<FP8, PS, true, QM>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
-  else segment_loop<FP8, PS, false, QM>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
+  const bool own_live = pair0 < npairs;
+  const bool partner_live = pb * PAIRS_BLOCK + (w ^ 1) * PAIRS_WAVE < npairs;
+  if (active && own_live && partner_live)
+    segment_loop<FP8, PS, true, QM, true, true>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
+  else if (active && own_live)
+    segment_loop<FP8, PS, true, QM, true, false>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
+  else if (active)
+    segment_loop<FP8, PS, true, QM, false, true>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
+  else segment_loop<FP8, PS, false, QM, false, false>(p, smem, b, L, t0, t1, qf, c, n_vis, min_vis, st, pw);
 
   // ---- segment end: the largest logit of the segment decides whether some
   // exponential went past the threshold; all waves idle on LDS; one flag per

@@ -135,9 +135,12 @@ def test_checker_finds_planted_hazards(decode_bodies):
     reg = f"{m.group(1)}{m.group(2)}"
     read = f"\tv_mov_b32_e32 v0, {reg}" if reg[0] == "v" else f"\tv_accvgpr_read_b32 v0, {reg}"
     assert ih.check_body(body[:i + 1] + [read] + body[i + 1:])
-    # the fences removed: results are read too early somewhere
-    stripped = [l for l in body if not re.match(r"\s*s_nop 7\s*$", l)]
-    assert ih.check_body(stripped)
+    # the fence's 12 wait states are what make the read safe: with them the read
+    # passes, with only the s_nop 3 left it is flagged (whether the compiled
+    # kernels still place a read inside that window depends on the schedule)
+    fenced = [body[i], "\ts_nop 7", "\ts_nop 3", read]
+    assert not ih.check_body(fenced)
+    assert ih.check_body([l for l in fenced if not re.match(r"\s*s_nop 7\s*$", l)])
     # a VALU write of an A operand right before the MFMA that reads it
     a_op = body[i].split(",")[1].strip()
     m = re.match(r"v\[(\d+)", a_op)
