@@ -344,6 +344,19 @@ void mla_decode_internal_set_grid_override(int32_t grid);
 void mla_decode_internal_set_segment_cost(int32_t tiles);
 
 /*
+ * Tuning hook, not part of the serving interface: with enable != 0 (the
+ * default), a fixed-shape launch whose requests each hold U = 2, 4 or 8
+ * 128-pair units (q_len_fixed x num_heads / 128, rounded up), on a grid whose
+ * workgroups per XCD are a multiple of U, hands each request's tiles to groups
+ * of U workgroups on one XCD that walk them together, one unit each, so that
+ * a KV tile is fetched from memory once per group and the other reads hit
+ * L2; 0 always splits unit by unit.  Changes how KV ranges are split and
+ * merged, never the result beyond rounding.  Affects later calls on every
+ * device; not thread-safe against concurrent launches.
+ */
+void mla_decode_internal_set_work_groups(int32_t enable);
+
+/*
  * Measurement hook, not part of the serving interface: when start_event and
  * stop_event are non-NULL, later mla_decode_paged calls record start_event (a
  * hipEvent_t) on their stream right before their first kernel and stop_event

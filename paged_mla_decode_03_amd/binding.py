@@ -92,6 +92,8 @@ def load_library():
     lib.mla_decode_internal_set_grid_override.restype = None
     lib.mla_decode_internal_set_segment_cost.argtypes = [i32]
     lib.mla_decode_internal_set_segment_cost.restype = None
+    lib.mla_decode_internal_set_work_groups.argtypes = [i32]
+    lib.mla_decode_internal_set_work_groups.restype = None
     lib.mla_decode_internal_set_kernel_events.argtypes = [vp, vp, vp]
     lib.mla_decode_internal_set_kernel_events.restype = None
     lib.mla_decode_internal_fp8_to_bf16.argtypes = [vp, vp, i64, vp]
@@ -177,6 +179,13 @@ def set_segment_cost(tiles):
     """Tuning hook: the work split's cost of a segment start, in tiles
     (negative restores the default)."""
     load_library().mla_decode_internal_set_segment_cost(int(tiles))
+
+
+def set_work_groups(enable):
+    """Tuning hook: let fixed-shape launches with 2, 4 or 8 units per request
+    walk each request's tiles with a group of workgroups (True, the default),
+    or always split unit by unit (False)."""
+    load_library().mla_decode_internal_set_work_groups(int(bool(enable)))
 
 
 def set_kernel_events(start_event, stop_event, decode_event=None):

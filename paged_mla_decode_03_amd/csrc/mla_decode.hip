@@ -139,6 +139,7 @@ struct Params {
   float bmm2;
   int32_t causal;
   int32_t seg_cost;  // cost of starting a segment, in tiles (see the work plan)
+  int32_t group;     // workgroups walking one cost range together (see the work plan), or 1
   const float* bmm1_dev;  // device bmm1_scale (replaces scale_log2 / LOG2E) or null
   const float* bmm2_dev;  // device bmm2_scale (replaces bmm2) or null
   const float* sinks;     // device [heads] sink logits (natural log) or null
@@ -362,7 +363,9 @@ __device__ __forceinline__ void lds_zero16(uint8_t* smem, uint32_t off) {
 
 // tile_off[b] = first linear tile of request b, tile_off[B] = total tiles;
 // unit_off[b] = first global unit of request b, unit_off[B] = total units.
-// A request contributes ceil(q_b*H / 128) units of ceil(L_b / 32) tiles each.
+// A request contributes ceil(q_b*H / 128) units of ceil(L_b / 32) tiles each;
+// with workgroup groups (p.group > 1) it is a single cost unit of
+// ceil(L_b / 32) tiles whose pair blocks the group's workgroups share out.
 // 128-pair units and 32-row tiles of request b (lengths outside the documented
 // ranges count as empty, so that the work walk always advances)
 __device__ __forceinline__ int request_units(const Params& p, int qb) { return max(0, ceil_div(qb * p.heads, PAIRS_BLOCK)); }
@@ -388,6 +391,7 @@ __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* s
     if (i < per && b0 + i < B) {
       int r0;
       u = request_units(p, request_rows(p, b0 + i, r0));
+      if (p.group > 1) u = min(u, 1);  // a request is one cost unit, walked by a whole group
       t = u * request_tiles(p, b0 + i);
     }
     t_b[i] = t;
@@ -1440,11 +1444,17 @@ void mla_decode_kernel(Params p) {
   const int S0 = p.seg_cost;
   // Cost space: unit u (request b, pair block pb) takes S0 + T_b consecutive
   // positions, S0 for the segment start it forces and then one per tile, so
-  // tile t of u sits at tile_off[b] + pb T_b + t + (u + 1) S0.  Workgroup g takes
-  // the positions [g C, (g + 1) C): equal cost, counting each extra segment.
+  // tile t of u sits at tile_off[b] + pb T_b + t + (u + 1) S0.  Cost range k
+  // takes the positions [k C, (k + 1) C): equal cost, counting each extra
+  // segment.  Normally each workgroup walks a range of its own.  With groups
+  // (a fixed query shape, every request U > 1 pair blocks) a cost unit is a
+  // whole request, and the U workgroups of a group, on one XCD, walk the same
+  // range together, workgroup j doing pair block j of each request: they read
+  // each KV tile at about the same time, so all but the first read hit L2.
   const int TC = uniform(tile_off[B] + unit_off[B] * S0);
   const int G = p.grid;
-  const int C = max(1, ceil_div(TC, G));
+  const int GU = p.group;
+  const int C = max(1, ceil_div(TC, G / GU));
   if (blockIdx.x == 0) {
     for (int b = threadIdx.x; b <= B; b += THREADS) {
       p.ws_plan[2 + b] = tile_off[b];
@@ -1458,7 +1468,9 @@ void mla_decode_kernel(Params p) {
   // Consecutive logical workgroups sit on one XCD (dispatch is round-robin over
   // the 8 XCDs), so workgroups sharing a request's KV share an L2.
   const int i = blockIdx.x;
-  const int g = (G % 8 == 0) ? ((i & 7) * (G >> 3) + (i >> 3)) : i;
+  const int gw = (G % 8 == 0) ? ((i & 7) * (G >> 3) + (i >> 3)) : i;
+  const int g = gw / GU;        // this workgroup's cost range
+  const int q = gw - g * GU;    // its pair block of every request in the range (groups)
   int x = g * C;
   const int end = min(TC, x + C);
   int b = 0, rel = 0;
@@ -1481,7 +1493,7 @@ void mla_decode_kernel(Params p) {
     int r0;
     const int qb = uniform(request_rows(p, b, r0));
     const int T = uniform(request_tiles(p, b));
-    const int units = uniform(request_units(p, qb));
+    const int units = uniform(GU > 1 ? min(request_units(p, qb), 1) : request_units(p, qb));  // cost units
     const int span = S0 + T;
     if (T == 0 || units == 0) {  // nothing to compute (lengths outside the contract)
       x += units * S0 - rel;
@@ -1500,11 +1512,12 @@ void mla_decode_kernel(Params p) {
     }
     const int t0 = r - S0;
     const int t1 = min(T, t0 + (end - x));
-    // segment (workgroup g, global unit u) has slot g + u: unique, since every
-    // later segment has a larger g or a larger u
-    const int slot = g + u_base + pb;
+    // segment (cost range g, cost unit u) has slot (g + u) GU + q: unique, since
+    // every later segment of a range has a larger g or a larger u, and the
+    // workgroups of a group differ in q
+    const int slot = (g + u_base + pb) * GU + q;
     float m_seed = -INFINITY;
-    while (!process_segment<FP8, PS, QM>(p, smem, b, pb, L, t0, t1, slot, m_seed)) {
+    while (!process_segment<FP8, PS, QM>(p, smem, b, GU > 1 ? q : pb, L, t0, t1, slot, m_seed)) {
     }
     x += t1 - t0;
     rel += t1 - t0;
@@ -1569,13 +1582,20 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int pb = pair / PAIRS_BLOCK;
   const int pl = pair - pb * PAIRS_BLOCK;
   const int T = max(0, ceil_div(L, TILE));
-  const int u = unit_off + pb;
-  const int U0 = tile_off + pb * T + (u + 1) * p.seg_cost;  // cost position of the unit's first tile
+  // with workgroup groups the request is one cost unit and pb picks the
+  // group member (slot offset q); otherwise pb is part of the cost position
+  const int GU = p.group;
+  const int pbc = GU > 1 ? 0 : pb;
+  const int q = pb - pbc;
+  const int u = unit_off + pbc;
+  const int U0 = tile_off + pbc * T + (u + 1) * p.seg_cost;  // cost position of the unit's first tile
   const int g0 = U0 / C;
   const int g1 = (U0 + T - 1) / C;
   const int nseg = (T > 0) ? g1 - g0 + 1 : 0;  // a request with no rows (a sequence shard may have none) has no segment
-  const float* mlb = p.ws_ml + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * 2;  // segment s at + s * PAIRS_BLOCK * 2
-  const uint16_t* ob = p.ws_o + ((size_t)(g0 + u) * PAIRS_BLOCK + pl) * D_V + 8 * lane;
+  // segment s of the unit (cost range g0 + s) has slot (g0 + s + u) GU + q
+  const size_t slot0 = (size_t)(g0 + u) * GU + q;
+  const float* mlb = p.ws_ml + (slot0 * PAIRS_BLOCK + pl) * 2;
+  const uint16_t* ob = p.ws_o + (slot0 * PAIRS_BLOCK + pl) * D_V + 8 * lane;
   // One round trip before any arithmetic: the O rows of the first MB segments
   // and the (max, sum) of the first 64 (one per lane) are all in flight
   // together; lane l holds dims 8l .. 8l + 8 of each O row.
@@ -1583,8 +1603,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   // a sink is one more softmax term with no value row: it joins the max and
   // the denominator
   const float sink = (p.sinks != nullptr) ? p.sinks[head] * LOG2E : -INFINITY;
-  const size_t o_step = (size_t)PAIRS_BLOCK * D_V;
-  const size_t ml_step = (size_t)PAIRS_BLOCK * 2;
+  const size_t o_step = (size_t)GU * PAIRS_BLOCK * D_V;
+  const size_t ml_step = (size_t)GU * PAIRS_BLOCK * 2;
   u32x4 o[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -1780,6 +1800,7 @@ constexpr int MAX_DEVICES = 64;
 std::atomic<int> g_cu_count[MAX_DEVICES];
 std::atomic<int> g_grid_override{0};
 std::atomic<int> g_seg_cost{-1};  // negative: the layout's default
+std::atomic<int> g_groups{1};     // 0: never walk a cost range with a group of workgroups
 std::atomic<void*> g_ev_start{nullptr};
 std::atomic<void*> g_ev_decode{nullptr};
 std::atomic<void*> g_ev_stop{nullptr};
@@ -1994,6 +2015,14 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   p.causal = causal ? 1 : 0;
   const int seg_cost = g_seg_cost.load(std::memory_order_relaxed);
   p.seg_cost = seg_cost >= 0 ? seg_cost : (sparse ? SEG_COST_SPARSE : SEG_COST_DEFAULT);
+  // A fixed query shape gives every request the same U pair blocks; for U = 2,
+  // 4 or 8, with U dividing the workgroups of each XCD, groups of U workgroups
+  // walk each request's tiles together (see the work plan in the kernel).
+  p.group = 1;
+  if (!sparse && qo_indptr == nullptr && g_groups.load(std::memory_order_relaxed) != 0) {
+    const int64_t U = ((int64_t)dims->q_len_fixed * dims->num_heads + PAIRS_BLOCK - 1) / PAIRS_BLOCK;
+    if ((U == 2 || U == 4 || U == 8) && grid % (8 * U) == 0) p.group = (int)U;
+  }
   p.bmm1_dev = opts ? opts->bmm1_scale : nullptr;
   p.bmm2_dev = opts ? opts->bmm2_scale : nullptr;
   // a sink is one softmax term per (row, head): in a sequence-sharded decode
@@ -2107,6 +2136,10 @@ void mla_decode_internal_set_grid_override(int32_t grid) { g_grid_override.store
 
 void mla_decode_internal_set_segment_cost(int32_t tiles) {
   g_seg_cost.store(tiles < 0 ? -1 : std::min(tiles, SEG_COST_MAX));
+}
+
+void mla_decode_internal_set_work_groups(int32_t enable) {
+  g_groups.store(enable != 0 ? 1 : 0);
 }
 
 void mla_decode_internal_set_kernel_events(void* start_event, void* decode_event, void* stop_event) {
