@@ -65,10 +65,10 @@ def _check_partial(got_o, got_l, ref_o, ref_l, what):
         check_close(got_l[~empty], ref_l[~empty], f"{what} lse")
 
 
-def _run_shards(kv_dtype, world, with_sinks):
+def _run_shards(kv_dtype, world, with_sinks, num_heads=32, q_len=3):
     fp8 = kv_dtype != "bf16"
     # short requests too, so that some ranks hold no visible row (or no row) of them
-    w = make_workload("dcp", seed=50 + world, seq_lens=[3, 5, 40, 333, 1200], num_heads=32, q_len=3,
+    w = make_workload("dcp", seed=50 + world, seq_lens=[3, 5, 40, 333, 1200], num_heads=num_heads, q_len=q_len,
                       page_size=32, kv_dtype=kv_dtype, kv_value_scale=0.5 if fp8 else 1.0,
                       bmm1_scale=INV_SQRT_192 * (0.02 if fp8 else 1.0), bmm2_scale=0.02 if fp8 else 1.0,
                       causal=True, want_lse=True)
@@ -115,6 +115,14 @@ def test_sequence_shards_match_oracle_and_merge_to_full(kv_dtype, world):
 def test_sequence_shards_with_sinks(kv_dtype):
     """Rank 0 carries the sinks; the merged ranks equal the full decode with sinks."""
     _run_shards(kv_dtype, 3, with_sinks=True)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3fn"])
+def test_sequence_shards_grouped_split(kv_dtype):
+    """128 heads x 2 rows: two units per request, so each rank's launch walks
+    every request with a pair of workgroups (the grouped split), including
+    ranks that hold no row of the short requests."""
+    _run_shards(kv_dtype, 8, with_sinks=True, num_heads=128, q_len=2)
 
 
 def test_single_rank_partial_equals_plain_decode():

@@ -1,7 +1,8 @@
 """Seeded random sweep over the option space against the float64 oracle:
 head counts, page sizes, fixed / packed queries, causal / dense, bf16 / fp8
-cache, fp8 query, sinks, LSE, forced grids and split costs, and the sparse
-top-k layout.  Every case is reproducible from its index."""
+cache, fp8 query, sinks, LSE, forced grids and split costs, grouped or
+unit-by-unit splits, and the sparse top-k layout.  Every case is reproducible
+from its index."""
 
 import os
 
@@ -26,6 +27,7 @@ def _reset_hooks():
     yield
     binding.set_grid_override(0)
     binding.set_segment_cost(-1)
+    binding.set_work_groups(True)
 
 
 def _case(i):
@@ -48,6 +50,11 @@ def _case(i):
     c["q8"] = c["fp8"] and not c["sparse"] and bool(rng.random() < 0.5)
     c["bmm1"] = float(rng.choice([0.02, 0.0722, 0.3]))
     c["bmm2"] = float(rng.choice([1.0, 0.5]))
+    # grids with whole groups of 2, 4 or 8 workgroups per XCD, and the groups
+    # switched off in some cases
+    if rng.random() < 0.3:
+        c["grid"] = int(rng.choice([16, 32, 64]))
+    c["groups"] = bool(rng.random() < 0.8)
     return c
 
 
@@ -62,6 +69,7 @@ def test_random_case(i):
                       bmm2_scale=c["bmm2"], causal=c["causal"], want_lse=c["lse"] or c["sparse"], **qlen)
     binding.set_grid_override(c["grid"])
     binding.set_segment_cost(c["seg"])
+    binding.set_work_groups(c["groups"])
     sinks = np.random.default_rng(3000 + i).uniform(-3.0, 5.0, c["H"]).astype(np.float32) if c["sinks"] else None
     s_t = None if sinks is None else torch.from_numpy(sinks).cuda()
     kv = torch.from_numpy(w.kv_bits)
