@@ -138,3 +138,42 @@ def test_packed_launch_is_never_grouped():
     plan = ws[:8].view(torch.int32).cpu().numpy()
     T = [-(-int(L) // TILE) for L in w.seq_lens]
     assert plan[1] == 2 * sum(T) + 2 * len(T) * 8
+
+
+def test_graph_replays_follow_length_updates_grouped():
+    """A grouped launch captured once: between replays eager work rewrites
+    seq_lens in place (within max_seq_len), which moves every range boundary of
+    the device-side split; each replay must equal an eager decode bitwise."""
+    w = _workload(128, 4, 64, "bf16", seed=81, batch=5, lens=(4, 1800))
+    t = to_device_tensors(w, "cuda")
+    B, H = w.batch, w.num_heads
+    q = t["q"].view(B, w.q_len_fixed, H, 576)
+    sl = t["seq_lens"]
+    nbytes = binding.workspace_bytes_for(q, t["kv"], t["block_tables"], sl, w.max_seq_len, return_lse=True)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, w.q_len_fixed, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, w.q_len_fixed, H), dtype=torch.float32, device="cuda")
+    kw = dict(return_lse=True, bmm1_scale=w.bmm1_scale, causal=True, out=out, lse=lse)
+    binding.decode(q, t["kv"], ws, t["block_tables"], sl, w.max_seq_len, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.decode(q, t["kv"], ws, t["block_tables"], sl, w.max_seq_len, **kw)
+    rng = np.random.default_rng(82)
+    full = w.seq_lens.astype(np.int64)
+    for rep in range(6):
+        # shorter lengths use a prefix of each request's pages: still valid
+        new = rng.integers(w.q_len_fixed, full, endpoint=True).astype(np.int32)
+        sl.copy_(torch.from_numpy(new).cuda())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        eo = torch.empty_like(out)
+        el = torch.empty_like(lse)
+        binding.decode(q, t["kv"], ws, t["block_tables"], sl, w.max_seq_len, return_lse=True,
+                       bmm1_scale=w.bmm1_scale, causal=True, out=eo, lse=el)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, eo) and torch.equal(got_l, el), rep
+        plan = ws[:8].view(torch.int32).cpu().numpy()
+        assert plan[1] == sum(-(-int(L) // TILE) for L in new) + B * 8
