@@ -345,14 +345,16 @@ void mla_decode_internal_set_segment_cost(int32_t tiles);
 
 /*
  * Tuning hook, not part of the serving interface: with enable != 0 (the
- * default), a fixed-shape launch whose requests each hold U = 2, 4 or 8
- * 128-pair units (q_len_fixed x num_heads / 128, rounded up), on a grid whose
- * workgroups per XCD are a multiple of U, hands each request's tiles to groups
- * of U workgroups on one XCD that walk them together, one unit each, so that
- * a KV tile is fetched from memory once per group and the other reads hit
- * L2; 0 always splits unit by unit.  Changes how KV ranges are split and
- * merged, never the result beyond rounding.  Affects later calls on every
- * device; not thread-safe against concurrent launches.
+ * default), a launch whose requests all hold the same number U = 2, 4 or 8 of
+ * 128-pair units (ceil(q_b x num_heads / 128); fixed-shape or packed), on a
+ * grid whose workgroups per XCD are a multiple of U, hands each request's
+ * tiles to a group of U workgroups on one XCD that walk them together, one
+ * unit each, so that a KV tile is fetched from memory once per group and the
+ * other reads hit L2.  The kernel decides this on the device from the
+ * lengths.  0 always splits unit by unit; the sparse top-k layout never
+ * groups.  Changes how KV ranges are split and merged, never the result
+ * beyond rounding.  Affects later calls on every device; not thread-safe
+ * against concurrent launches.
  */
 void mla_decode_internal_set_work_groups(int32_t enable);
 

@@ -182,9 +182,9 @@ def set_segment_cost(tiles):
 
 
 def set_work_groups(enable):
-    """Tuning hook: let fixed-shape launches with 2, 4 or 8 units per request
-    walk each request's tiles with a group of workgroups (True, the default),
-    or always split unit by unit (False)."""
+    """Tuning hook: let launches whose requests all hold the same 2, 4 or 8
+    units walk each request's tiles with a group of workgroups (True, the
+    default; decided on the device), or always split unit by unit (False)."""
     load_library().mla_decode_internal_set_work_groups(int(bool(enable)))
 
 

@@ -126,7 +126,7 @@ struct Params {
   float* lse;
   uint16_t* ws_o;   // [G + U][128][512] bf16 O per segment (unnormalised)
   float* ws_ml;     // [G + U][128][2]   per segment (max in log2 units, sum)
-  int32_t* ws_plan; // [0] = cost per workgroup C, [1] = total cost,
+  int32_t* ws_plan; // [0] = cost per range C, [1] = group size GU (1: none),
                     // [2 + b] = tile offset of request b (b <= B),
                     // [3 + B + b] = first global unit of request b (b <= B)
   int32_t batch;
@@ -139,7 +139,7 @@ struct Params {
   float bmm2;
   int32_t causal;
   int32_t seg_cost;  // cost of starting a segment, in tiles (see the work plan)
-  int32_t group;     // workgroups walking one cost range together (see the work plan), or 1
+  int32_t groups;    // nonzero: the plan may group workgroups (see the work plan)
   const float* bmm1_dev;  // device bmm1_scale (replaces scale_log2 / LOG2E) or null
   const float* bmm2_dev;  // device bmm2_scale (replaces bmm2) or null
   const float* sinks;     // device [heads] sink logits (natural log) or null
@@ -361,11 +361,15 @@ __device__ __forceinline__ void lds_zero16(uint8_t* smem, uint32_t off) {
 
 // ---------------------------------------------------------------- work plan
 
-// tile_off[b] = first linear tile of request b, tile_off[B] = total tiles;
-// unit_off[b] = first global unit of request b, unit_off[B] = total units.
-// A request contributes ceil(q_b*H / 128) units of ceil(L_b / 32) tiles each;
-// with workgroup groups (p.group > 1) it is a single cost unit of
-// ceil(L_b / 32) tiles whose pair blocks the group's workgroups share out.
+// tile_off[b] = first cost-space tile of request b, tile_off[B] = total tiles;
+// unit_off[b] = first cost unit of request b, unit_off[B] = total cost units.
+// A request contributes ceil(q_b*H / 128) units of ceil(L_b / 32) tiles each.
+// When every request has the same U units, U is 2, 4 or 8, U divides the
+// workgroups of each XCD and groups are allowed, the plan groups workgroups
+// (return value U): a request is then a single cost unit of ceil(L_b / 32)
+// tiles whose units the U workgroups of a group share out.  Otherwise it
+// returns 1 and each unit is a cost unit.  Every workgroup reaches the same
+// decision from the same lengths.
 // 128-pair units and 32-row tiles of request b (lengths outside the documented
 // ranges count as empty, so that the work walk always advances)
 __device__ __forceinline__ int request_units(const Params& p, int qb) { return max(0, ceil_div(qb * p.heads, PAIRS_BLOCK)); }
@@ -374,7 +378,7 @@ __device__ __forceinline__ int request_units(const Params& p, int qb) { return m
 __device__ __forceinline__ int req_len(const Params& p, int b) { return p.sparse_k > 0 ? p.sparse_k : p.seq_lens[b]; }
 __device__ __forceinline__ int request_tiles(const Params& p, int b) { return max(0, ceil_div(req_len(p, b), TILE)); }
 
-__device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* scan) {
+__device__ int build_plan(const Params& p, int* tile_off, int* unit_off, int* scan) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -384,61 +388,81 @@ __device__ void build_plan(const Params& p, int* tile_off, int* unit_off, int* s
   const int b0 = min(B, tid * per);
   // this thread's requests, kept in registers for the second pass
   int t_b[PER_MAX], u_b[PER_MAX];
-  int tiles = 0, units = 0;
+  // sums over this thread's requests for both layouts (unit by unit, and one
+  // cost unit per request), and the range of unit counts
+  int tiles = 0, units = 0, rtiles = 0, rcount = 0, umin = 0x7fffffff, umax = 0;
 #pragma unroll
   for (int i = 0; i < PER_MAX; ++i) {
     int t = 0, u = 0;
     if (i < per && b0 + i < B) {
       int r0;
       u = request_units(p, request_rows(p, b0 + i, r0));
-      if (p.group > 1) u = min(u, 1);  // a request is one cost unit, walked by a whole group
-      t = u * request_tiles(p, b0 + i);
+      t = request_tiles(p, b0 + i);
+      umin = min(umin, u);
+      umax = max(umax, u);
     }
     t_b[i] = t;
     u_b[i] = u;
-    tiles += t;
+    tiles += u * t;
     units += u;
+    rtiles += u > 0 ? t : 0;
+    rcount += u > 0 ? 1 : 0;
   }
   // inclusive prefix sums: within each wave by shuffles, then the four wave
-  // totals through LDS (one barrier)
-  int st = tiles, su = units;
+  // totals through LDS (one barrier); the unit-count range rides along
+  int v[4] = {tiles, units, rtiles, rcount};
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int vt = __shfl_up(st, off, 64);
-    const int vu = __shfl_up(su, off, 64);
-    if (lane >= off) {
-      st += vt;
-      su += vu;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int x = __shfl_up(v[k], off, 64);
+      if (lane >= off) v[k] += x;
     }
   }
-  int* wave_t = scan;
-  int* wave_u = scan + WAVES;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    umin = min(umin, __shfl_xor(umin, off, 64));
+    umax = max(umax, __shfl_xor(umax, off, 64));
+  }
   if (lane == 63) {
-    wave_t[w] = st;
-    wave_u[w] = su;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) scan[k * WAVES + w] = v[k];
+    scan[4 * WAVES + w] = umin;
+    scan[5 * WAVES + w] = umax;
   }
   __syncthreads();
-  int base_t = 0, base_u = 0;
-  for (int k = 0; k < w; ++k) {
-    base_t += wave_t[k];
-    base_u += wave_u[k];
+  int base[4] = {0, 0, 0, 0}, total[4] = {0, 0, 0, 0};
+  int gmin = 0x7fffffff, gmax = 0;
+  for (int k2 = 0; k2 < WAVES; ++k2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k2 < w) base[k] += scan[k * WAVES + k2];
+      total[k] += scan[k * WAVES + k2];
+    }
+    gmin = min(gmin, scan[4 * WAVES + k2]);
+    gmax = max(gmax, scan[5 * WAVES + k2]);
   }
-  int run_t = base_t + st - tiles;
-  int run_u = base_u + su - units;
+  const int U = gmax;
+  const int GU = (p.groups != 0 && gmin == gmax && (U == 2 || U == 4 || U == 8) && p.grid % (8 * U) == 0) ? U : 1;
+  const bool grouped = GU > 1;
+  int run_t = base[grouped ? 2 : 0] + v[grouped ? 2 : 0] - (grouped ? rtiles : tiles);
+  int run_u = base[grouped ? 3 : 1] + v[grouped ? 3 : 1] - (grouped ? rcount : units);
 #pragma unroll
   for (int i = 0; i < PER_MAX; ++i) {
     if (i < per && b0 + i < B) {
       tile_off[b0 + i] = run_t;
       unit_off[b0 + i] = run_u;
     }
-    run_t += t_b[i];
-    run_u += u_b[i];
+    const int uc = grouped ? min(u_b[i], 1) : u_b[i];
+    run_t += uc * t_b[i];
+    run_u += uc;
   }
   if (tid == THREADS - 1) {
-    tile_off[B] = base_t + st;
-    unit_off[B] = base_u + su;
+    tile_off[B] = total[grouped ? 2 : 0];
+    unit_off[B] = total[grouped ? 3 : 1];
   }
   __syncthreads();
+  return GU;
 }
 
 // ---------------------------------------------------------------- page-id window
@@ -1439,7 +1463,7 @@ void mla_decode_kernel(Params p) {
   // The plan lives in LDS only until this workgroup has found its starting point.
   int* tile_off = (int*)(smem + PLAN_SCRATCH_OFF);
   int* unit_off = (int*)(smem + UNIT_SCRATCH_OFF);
-  build_plan(p, tile_off, unit_off, (int*)(smem + SCAN_SCRATCH_OFF));
+  const int GU = uniform(build_plan(p, tile_off, unit_off, (int*)(smem + SCAN_SCRATCH_OFF)));
   const int B = p.batch;
   const int S0 = p.seg_cost;
   // Cost space: unit u (request b, pair block pb) takes S0 + T_b consecutive
@@ -1447,13 +1471,12 @@ void mla_decode_kernel(Params p) {
   // tile t of u sits at tile_off[b] + pb T_b + t + (u + 1) S0.  Cost range k
   // takes the positions [k C, (k + 1) C): equal cost, counting each extra
   // segment.  Normally each workgroup walks a range of its own.  With groups
-  // (a fixed query shape, every request U > 1 pair blocks) a cost unit is a
-  // whole request, and the U workgroups of a group, on one XCD, walk the same
+  // (GU > 1: every request holds the same GU pair blocks) a cost unit is a
+  // whole request, and the GU workgroups of a group, on one XCD, walk the same
   // range together, workgroup j doing pair block j of each request: they read
   // each KV tile at about the same time, so all but the first read hit L2.
   const int TC = uniform(tile_off[B] + unit_off[B] * S0);
   const int G = p.grid;
-  const int GU = p.group;
   const int C = max(1, ceil_div(TC, G / GU));
   if (blockIdx.x == 0) {
     for (int b = threadIdx.x; b <= B; b += THREADS) {
@@ -1462,7 +1485,7 @@ void mla_decode_kernel(Params p) {
     }
     if (threadIdx.x == 0) {
       p.ws_plan[0] = C;
-      p.ws_plan[1] = TC;
+      p.ws_plan[1] = GU;
     }
   }
   // Consecutive logical workgroups sit on one XCD (dispatch is round-robin over
@@ -1584,7 +1607,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void mla_merge_kernel(Params p) {
   const int T = max(0, ceil_div(L, TILE));
   // with workgroup groups the request is one cost unit and pb picks the
   // group member (slot offset q); otherwise pb is part of the cost position
-  const int GU = p.group;
+  const int GU = p.ws_plan[1];
   const int pbc = GU > 1 ? 0 : pb;
   const int q = pb - pbc;
   const int u = unit_off + pbc;
@@ -2015,14 +2038,9 @@ int mla_decode_paged_ex(const void* q, const void* kv_cache, const int32_t* bloc
   p.causal = causal ? 1 : 0;
   const int seg_cost = g_seg_cost.load(std::memory_order_relaxed);
   p.seg_cost = seg_cost >= 0 ? seg_cost : (sparse ? SEG_COST_SPARSE : SEG_COST_DEFAULT);
-  // A fixed query shape gives every request the same U pair blocks; for U = 2,
-  // 4 or 8, with U dividing the workgroups of each XCD, groups of U workgroups
-  // walk each request's tiles together (see the work plan in the kernel).
-  p.group = 1;
-  if (!sparse && qo_indptr == nullptr && g_groups.load(std::memory_order_relaxed) != 0) {
-    const int64_t U = ((int64_t)dims->q_len_fixed * dims->num_heads + PAIRS_BLOCK - 1) / PAIRS_BLOCK;
-    if ((U == 2 || U == 4 || U == 8) && grid % (8 * U) == 0) p.group = (int)U;
-  }
+  // The plan groups workgroups on the device when every request holds the
+  // same U = 2, 4 or 8 pair blocks (see the work plan in the kernel).
+  p.groups = (!sparse && g_groups.load(std::memory_order_relaxed) != 0) ? 1 : 0;
   p.bmm1_dev = opts ? opts->bmm1_scale : nullptr;
   p.bmm2_dev = opts ? opts->bmm2_scale : nullptr;
   // a sink is one softmax term per (row, head): in a sequence-sharded decode

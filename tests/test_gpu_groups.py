@@ -1,12 +1,12 @@
-"""GPU parity of the grouped work split: fixed-shape launches whose requests
-hold U = 2, 4 or 8 units of 128 (row, head) pairs hand each request's tiles to
-a group of U workgroups that walk them together, one unit each.
+"""GPU parity of the grouped work split: launches whose requests all hold the
+same U = 2, 4 or 8 units of 128 (row, head) pairs hand each request's tiles to
+a group of U workgroups that walk them together, one unit each.  The kernel
+decides this on the device, for fixed-shape and packed launches alike.
 
 Every case is checked against the float64 oracle on every request, with the
 groups on and off, at several grid sizes and segment-start costs.  The plan
 words the decode kernel leaves at the head of the workspace ([0] cost per
-range, [1] total cost) show which split ran: grouped, a request is one cost
-unit of T_b tiles; otherwise it is U units of T_b tiles each.
+range, [1] group size, 1 when not grouped) show which split ran.
 """
 
 import numpy as np
@@ -52,12 +52,15 @@ def _run(w):
     return o, l, plan
 
 
-def _expected_total_cost(w, grouped, seg_cost):
+def _cost_per_range(w, group, grid, seg_cost):
+    """The plan's cost per range C: total cost over the ranges (grid / group)."""
     T = [-(-int(L) // TILE) for L in w.seq_lens]
-    U = -(-w.q_len_fixed * w.num_heads // PAIRS)
-    if grouped:
-        return sum(T) + len(T) * seg_cost
-    return U * sum(T) + len(T) * U * seg_cost
+    units = [-(-int(q) * w.num_heads // PAIRS) for q in w.q_lens()]
+    if group > 1:
+        total = sum(T) + len(T) * seg_cost
+    else:
+        total = sum(u * t for u, t in zip(units, T)) + sum(units) * seg_cost
+    return max(1, -(-total // (grid // group)))
 
 
 CASES = [
@@ -93,7 +96,8 @@ def test_grouped_split_matches_oracle(case):
         for groups in (True, False):
             binding.set_work_groups(groups)
             o, l, plan = _run(w)
-            assert plan[1] == _expected_total_cost(w, groups, 8), (grid, groups, plan)
+            gu = U if groups else 1
+            assert plan[1] == gu and plan[0] == _cost_per_range(w, gu, grid or 256, 8), (grid, groups, plan)
             check_close(o[rows], ref_o[rows], f"{case} grid {grid} groups {groups} out")
             check_close(l[rows], ref_l[rows], f"{case} grid {grid} groups {groups} lse")
 
@@ -107,7 +111,7 @@ def test_grouped_split_segment_costs(cost):
     w = _workload(128, 4, 32, "bf16", seed=77, batch=9, lens=(4, 900))
     ref_o, ref_l, rows = oracle_rows(w, list(range(w.batch)))
     o, l, plan = _run(w)
-    assert plan[1] == _expected_total_cost(w, True, cost)
+    assert plan[1] == 4 and plan[0] == _cost_per_range(w, 4, 64, cost)
     check_close(o[rows], ref_o[rows], f"cost {cost} out")
     check_close(l[rows], ref_l[rows], f"cost {cost} lse")
 
@@ -119,25 +123,48 @@ def test_groups_need_whole_groups_per_xcd():
     w = _workload(128, 4, 64, "bf16", seed=78, batch=3, lens=(4, 1500))
     ref_o, ref_l, rows = oracle_rows(w, list(range(w.batch)))
     o, l, plan = _run(w)
-    assert plan[1] == _expected_total_cost(w, False, 8)
+    assert plan[1] == 1
     check_close(o[rows], ref_o[rows], "fallback out")
 
 
-def test_packed_launch_is_never_grouped():
-    """Packed (qo_indptr) launches keep the unit-by-unit split, whatever their
-    row counts."""
-    w = make_workload("packed", seed=79, batch=4, seq_len_range=(8, 800), num_heads=128, q_len_range=(2, 2),
-                      page_size=64, bmm1_scale=INV_SQRT_192, causal=True, want_lse=True)
+def _run_packed(w):
     t = to_device_tensors(w, "cuda")
     nbytes = binding.workspace_bytes_for(t["q"], t["kv"], t["block_tables"], t["seq_lens"], w.max_seq_len,
                                          qo_indptr=t["qo_indptr"], max_seq_len_q=w.max_q_len, return_lse=True)
-    ws = torch.zeros((nbytes,), dtype=torch.uint8, device="cuda")
-    binding.decode(t["q"], t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, qo_indptr=t["qo_indptr"],
-                   max_seq_len_q=w.max_q_len, return_lse=True, bmm1_scale=w.bmm1_scale, causal=True)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    o, l = binding.decode(t["q"], t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len,
+                          qo_indptr=t["qo_indptr"], max_seq_len_q=w.max_q_len, return_lse=True,
+                          bmm1_scale=w.bmm1_scale, causal=True)
     torch.cuda.synchronize()
     plan = ws[:8].view(torch.int32).cpu().numpy()
-    T = [-(-int(L) // TILE) for L in w.seq_lens]
-    assert plan[1] == 2 * sum(T) + 2 * len(T) * 8
+    H = w.num_heads
+    return o.float().reshape(w.total_q, H, 512).cpu().numpy(), l.reshape(w.total_q, H).cpu().numpy(), plan
+
+
+PACKED = [
+    # (H, q_b range, grouped): packed launches are grouped exactly when every
+    # request holds the same number of units
+    (128, (4, 4), 4),    # compact speculative 1+3
+    (16, (9, 16), 2),    # two units each, the second of 16..128 pairs
+    (128, (1, 3), 1),    # one to three units: not grouped
+    (64, (1, 2), 1),     # one unit each: nothing to group
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=[f"H{c[0]}-q{c[1][0]}to{c[1][1]}" for c in PACKED])
+def test_packed_launches(case):
+    H, qr, gu = case
+    w = make_workload("packed", seed=79 + H, batch=7, seq_len_range=(qr[1], 1500), num_heads=H, q_len_range=qr,
+                      page_size=64, bmm1_scale=INV_SQRT_192, causal=True, want_lse=True)
+    units = {-(-int(q) * H // PAIRS) for q in w.q_lens()}
+    assert (len(units) == 1) == (gu > 1 or units == {1})
+    ref_o, ref_l, rows = oracle_rows(w, list(range(w.batch)))
+    for grid in (0, 64):
+        binding.set_grid_override(grid)
+        o, l, plan = _run_packed(w)
+        assert plan[1] == gu, (grid, plan)
+        check_close(o[rows], ref_o[rows], f"packed {case} grid {grid} out")
+        check_close(l[rows], ref_l[rows], f"packed {case} grid {grid} lse")
 
 
 def test_graph_replays_follow_length_updates_grouped():
@@ -176,4 +203,43 @@ def test_graph_replays_follow_length_updates_grouped():
         torch.cuda.synchronize()
         assert torch.equal(got_o, eo) and torch.equal(got_l, el), rep
         plan = ws[:8].view(torch.int32).cpu().numpy()
-        assert plan[1] == sum(-(-int(L) // TILE) for L in new) + B * 8
+        assert plan[1] == 4 and plan[0] == -(-(sum(-(-int(L) // TILE) for L in new) + B * 8) // 64)
+
+
+def test_graph_replays_follow_qo_indptr_updates_grouped():
+    """A packed launch captured once: between replays eager work rewrites
+    qo_indptr in place (same total_q and max_q_len), switching the device-side
+    decision between grouped (every request 4 rows of 128 heads: 4 units) and
+    unit by unit (mixed unit counts); each replay equals an eager decode
+    bitwise."""
+    B, H, R, MQ = 6, 128, 24, 8
+    w = make_workload("gqo", seed=83, batch=B, seq_len_range=(MQ, 1400), num_heads=H, q_len_range=(4, 4),
+                      page_size=64, bmm1_scale=INV_SQRT_192, causal=True, want_lse=True)
+    assert w.total_q == R
+    t = to_device_tensors(w, "cuda")
+    qo = t["qo_indptr"]
+    nbytes = binding.workspace_bytes_for(t["q"], t["kv"], t["block_tables"], t["seq_lens"], w.max_seq_len,
+                                         qo_indptr=qo, max_seq_len_q=MQ, return_lse=True)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, H), dtype=torch.float32, device="cuda")
+    kw = dict(qo_indptr=qo, max_seq_len_q=MQ, return_lse=True, bmm1_scale=w.bmm1_scale, causal=True)
+    binding.decode(t["q"], t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.decode(t["q"], t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, out=out, lse=lse, **kw)
+    variants = [([4] * 6, 4), ([2, 6, 4, 4, 5, 3], 1), ([8, 8, 2, 2, 2, 2], 1), ([3, 5, 3, 5, 3, 5], 1), ([4] * 6, 4)]
+    for qb, gu in variants:
+        assert sum(qb) == R and max(qb) <= MQ
+        qo.copy_(torch.tensor(np.concatenate([[0], np.cumsum(qb)]), dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        plan = ws[:8].view(torch.int32).cpu().numpy()
+        assert plan[1] == gu, (qb, plan)
+        eo, el = torch.empty_like(out), torch.empty_like(lse)
+        binding.decode(t["q"], t["kv"], ws, t["block_tables"], t["seq_lens"], w.max_seq_len, out=eo, lse=el, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, eo) and torch.equal(got_l, el), qb
