@@ -14,7 +14,10 @@
 //     (tiles of 32 KV rows per "unit" = request x block of 128 (row, head)
 //     pairs), then owns an equal, contiguous range of a cost space that counts
 //     every tile and charges each segment start.  A unit cut by range
-//     boundaries is written as partials and merged by a second kernel.  No
+//     boundaries is written as partials and merged by a second kernel.  When
+//     every request holds the same 2, 4 or 8 units, a group of that many
+//     workgroups on one XCD walks each range together, one unit each, so a KV
+//     tile leaves HBM once per group and its other reads hit L2.  No
 //     device-to-host read anywhere.
 //   * QK^T: wave w owns 32 pairs with all 576 query dims in VGPRs (MFMA B
 //     operand) and computes S^T[32 tokens x 32 pairs] on
