@@ -275,6 +275,17 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
+// Elements j, j + 1 (j even) of a bf16x8 as one packed word, and the sum of
+// the two bf16 values of a packed word in fp32.
+__device__ __forceinline__ void put_p(bf16x8& v, int j, uint32_t word) {
+  u32x4 w = __builtin_bit_cast(u32x4, v);
+  w[j >> 1] = word;
+  v = __builtin_bit_cast(bf16x8, w);
+}
+__device__ __forceinline__ uint32_t get_p(const bf16x8& v, int j) { return __builtin_bit_cast(u32x4, v)[j >> 1]; }
+__device__ __forceinline__ float sum_bf16x2(uint32_t word) {
+  return __uint_as_float(word << 16) + __uint_as_float(word & 0xffff0000u);
+}
 
 // ---------------------------------------------------------------- matrix-core ops
 //
@@ -1039,13 +1050,12 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
         e[3] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[9 + j], c, nm));
         break;
       case 2:
-        pc0[j] = (__bf16)e[0];
-        pc0[j + 1] = (__bf16)e[1];
-        pc1[j] = (__bf16)e[2];
-        pc1[j + 1] = (__bf16)e[3];
+        put_p(pc0, j, pack_bf16x2(e[0], e[1]));
+        put_p(pc1, j, pack_bf16x2(e[2], e[3]));
         break;
       case 3: {
-        const float sm = (e[0] + e[1]) + (e[2] + e[3]);
+        // the denominator sums the same bf16 weights that P.V multiplies
+        const float sm = sum_bf16x2(get_p(pc0, j)) + sum_bf16x2(get_p(pc1, j));
         const float mx = fmaxf(fmaxf(s[j], s[j + 1]), fmaxf(s[8 + j], s[9 + j]));
         run_sum = (j == 0) ? sm : run_sum + sm;
         run_mx = (j == 0) ? mx : fmaxf(run_mx, mx);
@@ -1078,12 +1088,13 @@ __device__ __forceinline__ void segment_loop(const Params& p, uint8_t* smem, int
     st.m_max = fmaxf(st.m_max, mx);
     const float mbase = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e0 = __builtin_amdgcn_exp2f(s[j] - mbase);
-      const float e1 = __builtin_amdgcn_exp2f(s[8 + j] - mbase);
-      st.lsum += e0 + e1;
-      pc0[j] = (__bf16)e0;
-      pc1[j] = (__bf16)e1;
+    for (int j = 0; j < 8; j += 2) {
+      const uint32_t a = pack_bf16x2(__builtin_amdgcn_exp2f(s[j] - mbase), __builtin_amdgcn_exp2f(s[j + 1] - mbase));
+      const uint32_t b2 = pack_bf16x2(__builtin_amdgcn_exp2f(s[8 + j] - mbase),
+                                      __builtin_amdgcn_exp2f(s[9 + j] - mbase));
+      put_p(pc0, j, a);
+      put_p(pc1, j, b2);
+      st.lsum += sum_bf16x2(a) + sum_bf16x2(b2);  // the bf16 weights P.V multiplies
     }
     st.ref_ready = __builtin_amdgcn_ballot_w64(st.m_ref == -INFINITY) == 0;
   };
