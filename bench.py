@@ -18,8 +18,15 @@ between launches count), plus the decode kernel's own fraction from a
 separate pass with events inside each launch.  The float64 CPU oracle is
 timed on a bounded sample of the headline workload.
 
-  python bench.py [--gpus 1] [--steps 300] [--warmup 300] [--workload NAME]
-                  [--no-cpu-baseline] [--all]
+  python bench.py [--gpus 1] [--steps 300] [--warmup 300] [--settle-ms 100]
+                  [--workload NAME] [--no-cpu-baseline] [--all]
+
+Before the timed steps of each workload the device runs the warmup steps and
+then keeps stepping, untimed, until it has been busy for --settle-ms: after a
+load starts, the socket's power controller overshoots for a few tens of
+milliseconds (steps run 10-30% slow from about 3 to 40 ms in), and a short
+warmup would otherwise put the timed steps inside that transient.  The extra
+steps are reported under "settle".
 
 --workload NAME times that workload alone (a paged workload of
 paged_mla_decode_03_amd.inputs.WORKLOADS, the fp8-query one of Q8_WORKLOADS or
@@ -116,21 +123,34 @@ def profiled_traffic(workload):
     return int(total) if seen else None
 
 
-def time_steps(step, steps, warmup):
-    """Run warmup untimed steps, then time exactly `steps` steps, bracketed by
-    device synchronisation and by two HIP events on the launch stream (torch's
-    current stream, which the steps launch on), with nothing else inside the
-    region.  A second pass of as many steps (at most 500), outside the timed region, has the
+def time_steps(step, steps, warmup, settle_ms=0.0):
+    """Run warmup untimed steps, keep stepping (untimed) until the device has
+    been busy for settle_ms since the warmup began, then time exactly `steps`
+    steps, bracketed by device synchronisation and by two HIP events on the
+    launch stream (torch's current stream, which the steps launch on), with
+    nothing else inside the region.  The settle period exists because the
+    socket's power controller overshoots for a few tens of milliseconds after
+    a load starts (steps run 10-30% slow from about 3 to 40 ms in, then settle).
+    A second pass of as many steps (at most 500), outside the timed region, has the
     library record events inside every launch, before the decode kernel and
     right after it: those records add a few microseconds to a step, so they
     stay out of the timed one.  Returns (wall ms per step, device ms per step
-    over the timed region, mean decode-kernel ms)."""
+    over the timed region, mean decode-kernel ms, untimed settle steps)."""
     import numpy as np
     import torch
     from paged_mla_decode_03_amd import binding
     log(f"[bench] warmup {warmup}")
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         step()
+    settle = 0
+    while (time.perf_counter() - t_warm) * 1e3 < settle_ms:
+        for _ in range(16):
+            step()
+        settle += 16
+        torch.cuda.synchronize()
+    if settle:
+        log(f"[bench] settle: {settle} more untimed steps ({settle_ms:.0f} ms of load before timing)")
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     log(f"[bench] timing {steps} steps")
@@ -154,7 +174,7 @@ def time_steps(step, steps, warmup):
     torch.cuda.synchronize()
     binding.set_kernel_events(None, None)
     decode = float(np.mean([a.elapsed_time(b) for a, b, c in ev]))
-    return (t1 - t0) * 1e3 / steps, device_ms, decode
+    return (t1 - t0) * 1e3 / steps, device_ms, decode, settle
 
 
 def roofline(counts, kern_ms, name, q8=False):
@@ -202,10 +222,11 @@ def sparse_cpu_baseline(w, lists, budget_s=10.0):
                       f"in {dt:.1f} s, float64 NumPy"}
 
 
-def _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup, dtype, data, config, q8=False):
+def _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup, dtype, data, config, q8=False,
+            settle=None):
     roof = roofline(counts, device_ms, name, q8=q8)
     dec = roofline(counts, decode_ms, name, q8=q8)
-    return {
+    res = {
         "metric": METRIC,
         "value": counts["kv_tokens"] / (ms_step * 1e-3),
         "unit": "KV-tokens/s",
@@ -227,6 +248,9 @@ def _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup, dtype, d
         "kernel_source_sha256": kernel_source_sha256(),
         "roofline": roof,
     }
+    if settle is not None:
+        res["settle"] = settle  # the untimed steps run after the warmup (see time_steps)
+    return res
 
 
 def _dtype_label(kv_dtype, q8):
@@ -239,7 +263,7 @@ def _dtype_label(kv_dtype, q8):
             "P.V on bf16 MFMA (V widened exactly)")
 
 
-def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
+def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3, settle_ms=0.0):
     """One step = one sparse top-k decode call over the whole batch."""
     import torch
     from paged_mla_decode_03_amd import binding
@@ -275,7 +299,7 @@ def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
-    ms_step, device_ms, decode_ms = time_steps(step, steps, warmup)
+    ms_step, device_ms, decode_ms, settle = time_steps(step, steps, warmup, settle_ms)
     config = {"workload": name, "rows": w.total_q, "heads": w.num_heads, "top_k": K,
               "seq_lens": list(spec["seq_len_range"]), "page_size": w.page_size, "kv_dtype": w.kv_dtype,
               "lse": w.want_lse, "kv_tokens": counts["kv_tokens"]}
@@ -283,14 +307,14 @@ def run_sparse_workload(name, steps, warmup, want_cpu, rotate=3):
             f"{max(1, rotate)} cache copies rotated across steps)")
     res = _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup,
                   "bf16" if w.kv_dtype == "bf16" else "fp8 e4m3 KV widened exactly to bf16, bf16 MFMA",
-                  data, config)
+                  data, config, settle={"ms": settle_ms, "steps": settle})
     if want_cpu:
         log("[bench] cpu baseline (oracle)")
         res["cpu_baseline"] = sparse_cpu_baseline(w, lists)
     return res
 
 
-def run_workload(name, steps, warmup, want_cpu, rotate=3):
+def run_workload(name, steps, warmup, want_cpu, rotate=3, settle_ms=0.0):
     import torch
     from paged_mla_decode_03_amd import binding
     from paged_mla_decode_03_amd.inputs import (named_workload, to_device_tensors, WORKLOADS, Q8_WORKLOADS,
@@ -338,7 +362,7 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
         if rc != 0:
             raise RuntimeError(binding.mla_status_string(rc))
 
-    ms_step, device_ms, decode_ms = time_steps(step, steps, warmup)
+    ms_step, device_ms, decode_ms, settle = time_steps(step, steps, warmup, settle_ms)
     spec = WORKLOADS[base]
     config = {"workload": name, "batch": B, "heads": H, **({"q_dtype": "fp8_e4m3fn"} if q8 else {}),
               "q_len": spec.get("q_len") if "q_len_range" not in spec else list(spec["q_len_range"]),
@@ -349,7 +373,7 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
     data = (f"synthetic (seeded N(0,1) q/kv, shuffled pages; {max(1, rotate)} cache copies rotated across steps)"
             + ("; query rounded to fp8 E4M3FN, q_scale 1" if q8 else ""))
     res = _result(name, counts, ms_step, device_ms, decode_ms, steps, warmup, _dtype_label(w.kv_dtype, q8), data,
-                  config, q8=q8)
+                  config, q8=q8, settle={"ms": settle_ms, "steps": settle})
     if want_cpu:
         log("[bench] cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(w, q_codes=fp8_query_codes(w) if q8 else None)
@@ -359,8 +383,8 @@ def run_workload(name, steps, warmup, want_cpu, rotate=3):
 def _summary(r):
     """The per-workload figures carried under "configs" of the JSON line."""
     keep = ("value", "unit", "ms_per_step", "device_ms_per_step", "decode_kernel_ms", "decode_kernel_frac", "tflops",
-            "gbps", "dtype", "roofline")
-    d = {k: r[k] for k in keep}
+            "gbps", "dtype", "roofline", "settle")
+    d = {k: r[k] for k in keep if k in r}
     d["kv_tokens"] = r["config"]["kv_tokens"]
     return d
 
@@ -371,6 +395,10 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps first: the GPU reaches steady clocks only after tens of ms of work")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="after the warmup steps, keep stepping (untimed, reported as settle.steps) until the "
+                         "device has been busy this long: the socket's power controller overshoots for a few "
+                         "tens of ms after a load starts; 0 = warmup steps only")
     ap.add_argument("--workload", default=None, help="time this workload alone")
     ap.add_argument("--rotate", type=int, default=3,
                     help="copies of the KV cache and Q read in turn by consecutive steps (1 = one copy, which "
@@ -393,7 +421,7 @@ def main():
 
     def run(name, want_cpu):
         fn = run_sparse_workload if name in SPARSE_WORKLOADS else run_workload
-        return fn(name, args.steps, args.warmup, want_cpu, args.rotate)
+        return fn(name, args.steps, args.warmup, want_cpu, args.rotate, args.settle_ms)
 
     if args.workload is not None:
         res = run(args.workload, not args.no_cpu_baseline)

@@ -40,7 +40,7 @@ def test_result_carries_the_contract_fields(monkeypatch):
     monkeypatch.setattr(bench, "profiled_traffic", lambda name: 123)
     counts = {"bytes": 374.2e6, "flops": 86.2e9, "kv_tokens": 309371}
     r = bench._result("dsv3_bf16_decode", counts, 0.12, 0.118, 0.11, 300, 300, "bf16", "synthetic",
-                      {"workload": "dsv3_bf16_decode", "kv_tokens": 309371})
+                      {"workload": "dsv3_bf16_decode", "kv_tokens": 309371}, settle={"ms": 100.0, "steps": 528})
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
               "vs_baseline", "dtype", "data", "config", "roofline", "device_ms_per_step", "decode_kernel_ms",
               "decode_kernel_frac"):
@@ -52,6 +52,9 @@ def test_result_carries_the_contract_fields(monkeypatch):
     assert r["decode_kernel_frac"] == pytest.approx(374.2e6 / 0.11e-3 / 1e9 / PEAK_HBM_GBS)
     assert r["roofline"]["traffic"] == 123
     assert set(bench._summary(r)) >= {"value", "ms_per_step", "device_ms_per_step", "roofline", "kv_tokens"}
+    # the untimed settle steps after the warmup are reported, and the requested counts are kept as given
+    assert r["settle"] == {"ms": 100.0, "steps": 528} and bench._summary(r)["settle"]["steps"] == 528
+    assert r["steps"] == 300 and r["warmup"] == 300
 
 
 def test_profiled_traffic_sums_the_kernels_of_the_current_source(tmp_path, monkeypatch):
