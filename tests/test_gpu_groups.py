@@ -23,6 +23,11 @@ pytestmark = pytest.mark.gpu
 TILE, PAIRS = 32, 128
 
 
+def _cus():
+    """The default grid: one workgroup per compute unit."""
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
 @pytest.fixture(autouse=True)
 def _defaults():
     binding.set_grid_override(0)
@@ -96,8 +101,9 @@ def test_grouped_split_matches_oracle(case):
         for groups in (True, False):
             binding.set_work_groups(groups)
             o, l, plan = _run(w)
-            gu = U if groups else 1
-            assert plan[1] == gu and plan[0] == _cost_per_range(w, gu, grid or 256, 8), (grid, groups, plan)
+            G = grid or _cus()
+            gu = U if groups and G % (8 * U) == 0 else 1
+            assert plan[1] == gu and plan[0] == _cost_per_range(w, gu, G, 8), (grid, groups, plan)
             check_close(o[rows], ref_o[rows], f"{case} grid {grid} groups {groups} out")
             check_close(l[rows], ref_l[rows], f"{case} grid {grid} groups {groups} lse")
 
@@ -162,7 +168,8 @@ def test_packed_launches(case):
     for grid in (0, 64):
         binding.set_grid_override(grid)
         o, l, plan = _run_packed(w)
-        assert plan[1] == gu, (grid, plan)
+        G = grid or _cus()
+        assert plan[1] == (gu if G % (8 * gu) == 0 else 1), (grid, plan)
         check_close(o[rows], ref_o[rows], f"packed {case} grid {grid} out")
         check_close(l[rows], ref_l[rows], f"packed {case} grid {grid} lse")
 
@@ -203,7 +210,7 @@ def test_graph_replays_follow_length_updates_grouped():
         torch.cuda.synchronize()
         assert torch.equal(got_o, eo) and torch.equal(got_l, el), rep
         plan = ws[:8].view(torch.int32).cpu().numpy()
-        assert plan[1] == 4 and plan[0] == -(-(sum(-(-int(L) // TILE) for L in new) + B * 8) // 64)
+        assert plan[1] == 4 and plan[0] == -(-(sum(-(-int(L) // TILE) for L in new) + B * 8) // (_cus() // 4))
 
 
 def test_graph_replays_follow_qo_indptr_updates_grouped():
