@@ -2,7 +2,9 @@
 
 Produces paged_mla_decode_03_amd/libmla_decode.so from csrc/mla_decode.hip.
 Every HIP translation unit is compiled with packed-fp32 instruction selection
-disabled (the v_pk_*_f32 forms are avoided on this hardware).
+disabled (the v_pk_*_f32 forms are avoided on this hardware).  Also links the
+plain C++ test caller tests/c_caller/mla_c_caller against the library (host
+code only: the C header and HIP runtime calls).
 """
 
 import os
@@ -39,7 +41,27 @@ def build(verbose=False):
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, OUT)
+    build_c_caller(verbose)
     return OUT
+
+
+C_CALLER = os.path.join(ROOT, "tests", "c_caller", "mla_c_caller")
+
+
+def build_c_caller(verbose=False):
+    """Link the test caller of the C ABI (a plain host program) against the library."""
+    src = C_CALLER + ".cpp"
+    if not os.path.exists(src):
+        return None
+    cmd = [HIPCC, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), src, "-L", PKG, "-lmla_decode",
+           "-Wl,-rpath,$ORIGIN/../../paged_mla_decode_03_amd", "-o", C_CALLER + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the C caller ({res.returncode}):\n{res.stderr}")
+    os.replace(C_CALLER + ".tmp", C_CALLER)
+    return C_CALLER
 
 
 if __name__ == "__main__":
