@@ -32,6 +32,14 @@ def test_largest_batch():
     compare_with_oracle(w)
 
 
+def test_largest_batch_grouped():
+    """1024 requests of 2 rows x 128 heads: every request holds two units, so
+    the plan groups workgroups in pairs, over the largest batch."""
+    w = make_workload("maxb_g", seed=97, batch=MAX_BATCH, seq_len_range=(2, 60), num_heads=128, q_len=2,
+                      page_size=16, bmm1_scale=INV_SQRT_192, causal=True, want_lse=True)
+    compare_with_oracle(w)
+
+
 def test_every_request_one_row():
     """seq_len 1 everywhere: out = bmm2 * V[0] and lse = bmm1 * q.k[0] per (row, head)."""
     w = make_workload("len1", seed=91, seq_lens=[1] * 37, num_heads=32, q_len=1, page_size=32,
