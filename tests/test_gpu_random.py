@@ -20,6 +20,7 @@ from gpu_cases import check_close
 pytestmark = pytest.mark.gpu
 
 N_CASES = int(os.environ.get("MLA_RANDOM_CASES", "96"))
+FIRST_CASE = int(os.environ.get("MLA_RANDOM_FIRST", "0"))  # longer sweeps can start past the default cases
 
 
 @pytest.fixture(autouse=True)
@@ -58,7 +59,7 @@ def _case(i):
     return c
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", range(FIRST_CASE, FIRST_CASE + N_CASES))
 def test_random_case(i):
     c = _case(i)
     kv_dtype = "fp8_e4m3fn" if c["fp8"] else "bf16"
